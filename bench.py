@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE-layer forward pass on one MI355X.
+
+A step is one whole layer (router, top-k, dispatch, routed + shared experts,
+combine) over one batch of seeded synthetic tokens already resident in HBM.
+The default workload is the capacity/drop layer (N=16384, d=2048, 64 routed +
+1 shared SwiGLU experts of inner size 1408, top-2, softmax router with a Zipf
+logit skew, C = ceil(N*k/E)).
+
+Prints one JSON line: tokens/s, ms per step, the roofline entry of the
+dominant kernel (timed with HIP events on the library's stream over the timed
+region) and the float64 CPU oracle timed on a bounded sample on this host.
+Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0    # MI355X dense bf16 / fp16 matrix peak
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, A, touched, dtype_bytes=2):
+    """Algorithmic work of one layer step: (flops, bytes, gate_up_flops,
+    gate_up_bytes).  Flops: router 2NdE + per kept assignment 6dI (SwiGLU) or
+    4dI (ReLU) + the same per token for each shared expert.  Bytes: the weights
+    of every touched expert and the shared experts, the router matrix, x read
+    once and y (fp32) written once."""
+    m = 3 if w.activation == "swiglu" else 2
+    rows = A + w.N * w.S
+    flops = 2 * w.N * w.d * w.E + 2 * m * w.d * w.I * rows
+    wbytes = m * w.d * w.I * dtype_bytes
+    nbytes = ((touched + w.S) * wbytes + w.d * w.E * dtype_bytes + w.N * w.d * dtype_bytes
+              + w.N * w.d * 4)
+    gu_mats = m - 1
+    gu_flops = 2 * gu_mats * w.d * w.I * rows
+    # gate/up launch: its weights (touched + shared), the gathered x rows, h (fp16) written
+    gu_bytes = ((touched + w.S) * gu_mats * w.d * w.I * dtype_bytes + rows * w.d * dtype_bytes
+                + rows * w.I * 2)
+    return flops, nbytes, gu_flops, gu_bytes
+
+
+def cpu_baseline(w, inp, budget_s=15.0):
+    """Time the float64 oracle (as it is) on a bounded sample of the workload:
+    routing + dispatch of the whole batch, expert FFNs for a prefix of tokens.
+    Returns the dict for the JSON line."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        blas = ",".join(sorted({f"{i.get('internal_api')}" for i in info}))
+    except Exception:  # pragma: no cover
+        threads, blas = len(os.sched_getaffinity(0)), "unknown"
+    x = synth.to_f64(w, inp.x)
+    wr = synth.to_f64(w, inp.w_router)
+    lb = None if inp.logit_bias is None else inp.logit_bias.astype(np.float64)
+    sb = None if inp.sel_bias is None else inp.sel_bias.astype(np.float64)
+    cache = {}
+
+    def get(e, shared=False):
+        key = (shared, e)
+        if key not in cache:
+            arrs = inp.shared(e) if shared else inp.expert(e)
+            cache[key] = tuple(None if a is None else synth.to_f64(w, a) for a in arrs)
+        return cache[key]
+
+    t0 = time.perf_counter()
+    r = O.route(x, wr, w.k, w.gating, lb, sb, inp.modality)
+    disp = O.dispatch(r["idx"], w.E, O.capacity(w.f, w.N, w.k, w.E), inp.modality)
+    t_route = time.perf_counter() - t0
+    # warm the per-expert float64 weights outside the timed FFN sample
+    for e in range(w.E):
+        get(e)
+    for s in range(w.S):
+        get(s, True)
+
+    def ffn_time(n):
+        toks = np.arange(n)
+        t = time.perf_counter()
+        O.forward(x, w.k, w.E, w.gating, w.activation, get_expert=get, n_shared=w.S,
+                  get_shared=lambda s: get(s, True), w_router=wr, clip=w.clip, f=w.f,
+                  logit_bias=lb, sel_bias=sb, modality=inp.modality, forced_idx=r["idx"],
+                  tokens=toks)
+        return time.perf_counter() - t
+
+    n = min(w.N, 128)
+    t_probe = ffn_time(n)
+    # forward(tokens=...) also re-routes the whole batch: subtract that part
+    per_tok = max(t_probe - t_route, 1e-6) / n
+    n2 = int(min(w.N, max(n, budget_s / per_tok)))
+    t_ffn = ffn_time(n2)
+    t_tok = max(t_ffn - t_route, 1e-9) / n2 + t_route / w.N
+    return {"value": 1.0 / t_tok, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"float64 NumPy oracle ({blas} BLAS): routing + dispatch of all {w.N} "
+                       f"tokens ({t_route:.2f} s) and expert FFNs + combine for the first {n2} "
+                       f"tokens ({t_ffn - t_route:.2f} s); value = 1 / (route time per token + "
+                       f"FFN time per sampled token)"),
+            "host_cpu_count": len(os.sched_getaffinity(0))}
+
+
+def pmc_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM traffic of one launch from a committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("source_sha256") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="cap")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs the MoE layer on exactly one GPU; multi-GPU runs (expert or "
+              "token sharding over xGMI) are not built. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from synth import device as sdev
+    from mixture_experts_layer_16_amd import _lib as L
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = synth.get(args.workload)
+    log(f"workload {w.name}: N={w.N} d={w.d} E={w.E}+{w.S} k={w.k} I={w.I} f={w.f}")
+    t = time.perf_counter()
+    inp = synth.make_inputs(w)
+    di = sdev.upload(inp)
+    log(f"inputs generated and uploaded in {time.perf_counter() - t:.1f} s")
+
+    p = L.problem(w.N, w.d, w.E, w.k, w.I, S=w.S, gating=w.gating, activation=w.activation,
+                  dtype=w.dtype, n_bias_sets=w.n_bias_sets, act_clip=w.clip,
+                  capacity_factor=w.f)
+    ws = L.workspace(p)
+    y = torch.empty((w.N, w.d), dtype=torch.float32, device="cuda")
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    rout = L.routing(offsets=offsets, counts=counts)
+    wts = L.weights(di.w_router, di.w_gate, di.w_up, di.w_down, di.ws_gate, di.ws_up, di.ws_down)
+    stream = torch.cuda.current_stream()
+
+    def step(profile=None):
+        L.moe_forward(p, wts, di.x, di.logit_bias, di.sel_bias, di.modality, y, rout, ws,
+                      stream=stream, profile=profile)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    # timed region: K steps; the gate/up GEMM (dominant kernel) is bracketed by
+    # HIP events recorded on the same stream by the library
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    profs = [L.profile({("gate_up", 0): a, ("gate_up", 1): b}) for a, b in evs]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(profs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    ms_step_ev = e0.elapsed_time(e1) / K
+    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    log(f"timed {K} steps: {ms_step:.4f} ms/step wall, {ms_step_ev:.4f} ms/step events, "
+        f"gate/up {gu_ms:.4f} ms")
+
+    # per-stage breakdown (separate, untimed-for-value pass)
+    stage_ev = {(s, j): torch.cuda.Event(enable_timing=True) for s in L.STAGES for j in (0, 1)}
+    for ev in stage_ev.values():
+        ev.record(stream)
+    torch.cuda.synchronize()
+    sprof = L.profile(stage_ev)
+    reps = 10
+    acc = {s: 0.0 for s in L.STAGES}
+    for _ in range(reps):
+        step(sprof)
+        torch.cuda.synchronize()
+        for s in L.STAGES:
+            acc[s] += stage_ev[(s, 0)].elapsed_time(stage_ev[(s, 1)]) / reps
+    log("stages ms: " + ", ".join(f"{s}={v:.4f}" for s, v in acc.items()))
+
+    off = offsets.cpu().numpy()
+    A = int(off[-1])
+    touched = int(np.count_nonzero(np.diff(off)))
+    flops, nbytes, gu_flops, gu_bytes = algorithmic(w, A, touched,
+                                                    dtype_bytes=2 if w.dtype == "bf16" else 4)
+    tokens_s = w.N / (ms_step * 1e-3)
+    layer_tflops = flops / (ms_step * 1e-3) / 1e12
+    layer_gbs = nbytes / (ms_step * 1e-3) / 1e9
+    decode = w.N <= 64
+    src = open(os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc", "gemm.hip"), "rb").read()
+    src_hash = hashlib.sha256(src).hexdigest()
+    kname = "ffn_gemm_bf16_gate_up"
+    traffic = pmc_traffic(kname, w.name, src_hash)
+    if decode:
+        ach = gu_bytes / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "traffic": traffic}
+    else:
+        ach = gu_flops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_MFMA_TFLOPS, "traffic": traffic}
+    roof["kernel"] = kname
+    roof["ms_per_launch"] = gu_ms
+    roof["algorithmic_per_launch"] = gu_bytes if decode else gu_flops
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, inp, args.cpu_budget)
+        log(f"cpu oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "MoE-layer tokens/s at 1 GPU",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; random-init weights of the stated shapes)",
+        "config": {"workload": w.name, "N": w.N, "d": w.d, "E": w.E, "S": w.S, "k": w.k,
+                   "I": w.I, "capacity_factor": w.f, "gating": w.gating,
+                   "activation": w.activation, "kept_assignments": A,
+                   "touched_experts": touched},
+        "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / PEAK_MFMA_TFLOPS,
+                  "gbs": layer_gbs, "hbm_frac": layer_gbs / PEAK_HBM_GBS,
+                  "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                  "ms_per_step_events": ms_step_ev},
+        "stages_ms": acc,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

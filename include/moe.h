@@ -1,0 +1,238 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts FFN layer forward pass.
+ *
+ * The layer (one MoE FFN, per token t of a flattened batch x[N][d]):
+ *   z_t   = x_t W_g + o                       router logits, one per expert
+ *   s_t   = softmax(z_t) | sigmoid(z_t)       scores
+ *   key_t = z_t + b   (softmax) | s_t + b[m_t]  (sigmoid)   selection keys
+ *   T_t   = the k largest keys, descending, equal keys -> lower expert index
+ *   g_tj  = s_tj / sum_{i in T_t} s_ti        renormalised gate weights (no bias)
+ *   per expert e the first C tokens in token order are kept, the rest dropped
+ *   y_t   = sum_{j kept} g_tj FFN_{e_tj}(x_t) + sum_s FFN_shared_s(x_t)
+ *   FFN   = (silu(x W_gate) * (x W_up), clamped to +-act_clip) W_down   (SwiGLU)
+ *         | max(x W1, 0) W2                                             (ReLU)
+ *
+ * Sources of each step (page title, section):
+ *   router, softmax, top-k, renormalisation, combine:
+ *       "Основы MoE" (ai.flicky.cc), section "Как устроен MoE-слой", steps 1-4;
+ *   tie rule (lower index first): same page, section "Практика" (topk_route);
+ *   selection bias on the choice only:
+ *       "Le groupe d'experts (MoE)" (aiengineeringfromscratch.com), "Étape 1: le routeur";
+ *       "Mixture-of-Experts" (mkdocs.reaper.mx, DeepSeek-V4.1-Flash), "L'équilibrage de charge";
+ *   one bias set per modality: same V4.1 page, "La nouveauté de V4.1 : l'équilibrage par modalité";
+ *   capacity C = ceil(N*k/E * f), token-order drops, shared expert outside the
+ *   renormalisation: "Mixture-of-Experts : routage et capacité" (cours.spawnkit.ai),
+ *       "L'idée — Capacité", "Cas guidé — trace complète", "L'idée — Top-k et mélange";
+ *   SwiGLU with three matrices, clip at 10: V4.1 page, table "Les chiffres de
+ *       DeepSeek-V4.1-Flash" and "Le compte des paramètres";
+ *   two-layer ReLU expert: "Mixture of Experts" fiche (dataistudio.com), code section.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers marked (device) are HIP device pointers; (host) are host pointers.
+ * - All device work is enqueued asynchronously on `stream` (a hipStream_t; NULL =
+ *   the null stream).  Nothing synchronises; buffers must stay alive until the
+ *   stream work completes.  The library never allocates, frees or keeps a pointer
+ *   past the call; the caller owns every buffer.
+ * - Inputs x and all weights are bfloat16 (raw 16-bit words) when p->dtype ==
+ *   MOE_BF16 and float32 when p->dtype == MOE_F32.  Router logit offsets and
+ *   selection biases are always float32; gate weights are float32.
+ * - The layer output y is float32 [N][d] for both dtypes (sums are kept in
+ *   float32 and not rounded to 16 bits).
+ * - Expert output rows ("y_rows", between moe_expert_ffn and moe_combine) are
+ *   IEEE fp16 when p->dtype == MOE_BF16 and float32 when MOE_F32.  Internally
+ *   the hidden activation h is fp16 as well and the down projection runs on
+ *   the fp16 matrix cores, with the bf16 W_down converted exactly to fp16.
+ * - Weight layout is [out][in] (each row is one output unit, contiguous along
+ *   the reduction dimension): router [E][d]; gate/up [E][I][d]; down [E][d][I];
+ *   shared experts [S][I][d] and [S][d][I].  For ReLU experts w_gate is NULL,
+ *   w_up = W1^T and w_down = W2^T.
+ * - Assignment arrays are flat [N*k] in token-major order (a = t*k + j).
+ * - Return value: MOE_OK or a negative status (see moe_status_string).
+ *   Validation happens on the host before any launch; a failed call enqueues
+ *   nothing.  Device faults surface at the caller's next synchronisation.
+ *   Capacity overflow is NOT an error: it is the drop policy.  N == 0 is a
+ *   successful no-op.
+ * - Calls are reentrant; overlapping calls must use distinct workspaces.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,          /* a required pointer is NULL */
+  MOE_ERR_INVALID = -2,       /* a size or option is out of range */
+  MOE_ERR_UNSUPPORTED = -3,   /* valid but not supported (alignment, dtype mix) */
+  MOE_ERR_WORKSPACE = -4,     /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_HIP = -5            /* a kernel launch failed (hipGetLastError) */
+};
+
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_gating;
+typedef enum { MOE_SWIGLU = 0, MOE_RELU = 1 } moe_activation;
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+/* The problem: the arguments of the layer.  Passed by pointer, read only. */
+typedef struct {
+  int64_t n_tokens;        /* N >= 0 tokens (rows of x) */
+  int32_t d_model;         /* d >= 1; multiple of 8 for MOE_BF16 */
+  int32_t n_experts;       /* E routed experts, 1..1024 */
+  int32_t top_k;           /* k experts per token, 1..min(E, 32) */
+  int32_t d_expert;        /* I expert inner size; multiple of 8 for MOE_BF16 */
+  int32_t n_shared;        /* S >= 0 always-on shared experts (inner size I), <= 8 */
+  int32_t gating;          /* moe_gating */
+  int32_t activation;      /* moe_activation */
+  int32_t dtype;           /* moe_dtype of x and the weights */
+  int32_t n_bias_sets;     /* 0: no selection bias; 1: bias[E]; 2: bias[2][E] by modality */
+  int32_t renormalize;     /* must be 1: gate weights renormalised over the k chosen */
+  float act_clip;          /* > 0: clamp silu(a)*u to [-act_clip, act_clip]; 0: none */
+  double capacity_factor;  /* f > 0: C = ceil(N*k/E * f) (exact); <= 0: unlimited */
+} moe_problem;
+
+/* Expert weights (device).  Routed experts are required; shared ones when S > 0. */
+typedef struct {
+  const void* w_router;    /* [E][d] */
+  const void* w_gate;      /* [E][I][d]; NULL for MOE_RELU */
+  const void* w_up;        /* [E][I][d] */
+  const void* w_down;      /* [E][d][I] */
+  const void* ws_gate;     /* [S][I][d]; NULL for MOE_RELU or S == 0 */
+  const void* ws_up;       /* [S][I][d]; NULL when S == 0 */
+  const void* ws_down;     /* [S][d][I]; NULL when S == 0 */
+} moe_weights;
+
+/* Optional routing outputs of moe_forward (device pointers, each may be NULL). */
+typedef struct {
+  int32_t* topk_idx;         /* [N*k] */
+  float* topk_w;             /* [N*k] */
+  int32_t* counts;           /* [E]   demand per expert (before capacity) */
+  int32_t* modality_counts;  /* [2][E] demand per modality (n_bias_sets == 2 only) */
+  int32_t* offsets;          /* [E+1] prefix sums of kept counts */
+  int32_t* row_of;           /* [N*k] slot row, -1 if dropped */
+  int32_t* token_of_row;     /* [N*k] valid in [0, offsets[E]) */
+  uint8_t* drop_mask;        /* [N*k] 1 if dropped */
+  double* logits;            /* [N][E] router logits z (float64) */
+} moe_routing;
+
+/* Bytes of device workspace any call below needs for problem p (host). */
+int moe_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* Capacity C = ceil(f * N * k / E) computed exactly on the binary value of f;
+ * C >= 1 when f > 0; *C = -1 when unlimited (host).  Routing and capacity
+ * slides: "L'idée — Capacité". */
+int moe_capacity(const moe_problem* p, int64_t* C);
+
+/* Parameter counts of one layer (host): expert_total = (E+S)*m*d*I and
+ * expert_active = (k+S)*m*d*I with m = 3 (SwiGLU) or 2 (ReLU); router = d*E.
+ * "Основы MoE", section "Всего параметров и активных параметров". */
+int moe_param_counts(const moe_problem* p, int64_t* expert_total,
+                     int64_t* expert_active, int64_t* router);
+
+/* Router + scoring + top-k + gate weights (steps 1-3 of "Как устроен MoE-слой").
+ *   x         (device) [N][d]
+ *   w_router  (device) [E][d]
+ *   logit_bias(device, nullable) float32 [E]: added to the logits; moves both
+ *             the choice and the weights.
+ *   sel_bias  (device, nullable unless n_bias_sets > 0) float32 [n_bias_sets][E]:
+ *             moves only the choice.
+ *   modality  (device) uint8 [N], 0 = text, 1 = image; required iff n_bias_sets == 2.
+ *   topk_idx  (device) int32 [N*k] out: descending key order, ties -> lower index.
+ *   topk_w    (device) float32 [N*k] out: renormalised unbiased scores, sum 1.
+ *   logits    (device, nullable) float64 [N][E] out: z.
+ * Logits are accumulated with float64 folding of short matrix-core partials,
+ * so the chosen set is the float64 one except for keys closer than ~1e-7 of
+ * their scale. */
+int moe_route(const moe_problem* p, const void* x, const void* w_router,
+              const float* logit_bias, const float* sel_bias, const uint8_t* modality,
+              int32_t* topk_idx, float* topk_w, double* logits,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Histogram, capacity and token-order permutation (routing slides, "Cas guidé
+ * — trace complète").  Deterministic: ranks follow token order.
+ *   topk_idx        (device) int32 [N*k] in
+ *   modality        (device, nullable) uint8 [N]; with modality_counts
+ *   counts          (device) int32 [E] out: demand per expert
+ *   modality_counts (device, nullable) int32 [2][E] out
+ *   offsets         (device) int32 [E+1] out: exclusive prefix sums of min(count, C)
+ *   row_of          (device) int32 [N*k] out: offsets[e] + rank, or -1 if dropped
+ *   token_of_row    (device) int32 [N*k] out: token of each kept row, [0, offsets[E])
+ *   drop_mask       (device) uint8 [N*k] out */
+int moe_permute(const moe_problem* p, const int32_t* topk_idx, const uint8_t* modality,
+                int32_t* counts, int32_t* modality_counts, int32_t* offsets,
+                int32_t* row_of, int32_t* token_of_row, uint8_t* drop_mask,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs over grouped rows.
+ * Routed mode (token_of_row != NULL): for each expert e, rows
+ *   [offsets[e], offsets[e+1]) take x[token_of_row[row]] and y_rows[row] =
+ *   FFN_e(x[token]).  Weights are the routed [E][..] tensors.
+ * Dense mode (token_of_row == NULL, offsets == NULL): one expert (w_gate [I][d],
+ *   w_up [I][d], w_down [d][I]) over all N rows: y_rows[t] = FFN(x[t]) -- the
+ *   shared expert.
+ *   y_rows (device) [N*k][d] (routed) or [N][d] (dense), row format (fp16 for
+ *          MOE_BF16, float32 for MOE_F32). */
+int moe_expert_ffn(const moe_problem* p, const void* x, const int32_t* token_of_row,
+                   const int32_t* offsets, const void* w_gate, const void* w_up,
+                   const void* w_down, void* y_rows, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Gate-weighted combine and un-permute ("Как устроен MoE-слой", step 4):
+ *   y[t] = sum_{j: row_of[t*k+j] >= 0} topk_w[t*k+j] * y_rows[row_of[t*k+j]]
+ *          + sum_s y_shared[s][t]
+ * summed in float32 in that fixed order.  Dropped slots add nothing and the
+ * other weights are not renormalised.
+ *   y_rows   (device) [*][d] row format; row_of, topk_w (device) [N*k];
+ *   y_shared (device, nullable) [S][N][d] row format; y (device) float32 [N][d] out. */
+int moe_combine(const moe_problem* p, const void* y_rows, const int32_t* row_of,
+                const float* topk_w, const void* y_shared, void* y, void* stream);
+
+/* The whole layer: route, permute, routed + shared experts, combine; y is
+ * float32 [N][d].  Equal to the staged calls.  routing_out (host struct of device pointers, nullable)
+ * receives the intermediate routing arrays for verification. */
+int moe_forward(const moe_problem* p, const moe_weights* w, const void* x,
+                const float* logit_bias, const float* sel_bias, const uint8_t* modality,
+                void* y, const moe_routing* routing_out, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* Stages of moe_forward, in launch order (indices into moe_profile.ev). */
+enum {
+  MOE_STAGE_ROUTE = 0,      /* router GEMM + top-k */
+  MOE_STAGE_PERMUTE = 1,    /* rank, scan, scatter */
+  MOE_STAGE_PLAN = 2,       /* grouped-GEMM tile plan */
+  MOE_STAGE_GATE_UP = 3,    /* gate/up grouped GEMM + activation */
+  MOE_STAGE_DOWN = 4,       /* down grouped GEMM */
+  MOE_STAGE_COMBINE = 5,    /* weighted combine + un-permute */
+  MOE_NUM_STAGES = 6
+};
+
+/* Measurement hook: hipEvent_t handles recorded on the stream immediately
+ * before (ev[2*i]) and after (ev[2*i+1]) stage i; NULL entries are skipped.
+ * The caller creates, owns and reads the events. */
+typedef struct {
+  void* ev[2 * MOE_NUM_STAGES];
+} moe_profile;
+
+/* moe_forward with an optional measurement hook (prof may be NULL; then it is
+ * exactly moe_forward).  Recording events adds stream markers between the
+ * stages and nothing else. */
+int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
+                   const float* logit_bias, const float* sel_bias, const uint8_t* modality,
+                   void* y, const moe_routing* routing_out, const moe_profile* prof,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Text of a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,391 @@
+// C-ABI entry points: host-side validation, exact capacity, workspace layout
+// and the launch sequence of each stage.  No allocation, no synchronisation.
+#include <math.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const moe_problem* p) {
+  const size_t N = (size_t)p->n_tokens, E = (size_t)p->n_experts, k = (size_t)p->top_k;
+  const size_t S = (size_t)p->n_shared, d = (size_t)p->d_model, I = (size_t)p->d_expert;
+  const size_t esz = p->dtype == MOE_BF16 ? 2 : 4;
+  const size_t nk = N * k;
+  const size_t nblk = (size_t)perm_blocks((int64_t)N);
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes ? bytes : 1);
+    return o;
+  };
+  L.logits = take(N * E * 8);
+  L.topk_idx = take(nk * 4);
+  L.topk_w = take(nk * 4);
+  L.counts = take(E * 4);
+  L.mod_counts = take(2 * E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.row_of = take(nk * 4);
+  L.token_of_row = take(nk * 4);
+  L.drop = take(nk);
+  L.lrank = take(nk * 4);
+  L.blk_counts = take(nblk * 3 * E * 4);
+  L.plan = take((3 * (E + S) + 4) * 4);
+  L.h = take((nk + N * S) * I * esz);
+  L.yrows = take((nk + N * S) * d * esz);
+  L.total = off;
+  return L;
+}
+
+static int validate(const moe_problem* p) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->n_tokens < 0 || p->n_tokens > (int64_t(1) << 24)) return MOE_ERR_INVALID;
+  if (p->d_model < 1 || p->d_expert < 1) return MOE_ERR_INVALID;
+  if (p->n_experts < 1 || p->n_experts > kMaxExperts) return MOE_ERR_INVALID;
+  if (p->top_k < 1 || p->top_k > p->n_experts || p->top_k > kMaxTopK) return MOE_ERR_INVALID;
+  if (p->n_shared < 0 || p->n_shared > kMaxShared) return MOE_ERR_INVALID;
+  if (p->gating != MOE_SOFTMAX && p->gating != MOE_SIGMOID) return MOE_ERR_INVALID;
+  if (p->activation != MOE_SWIGLU && p->activation != MOE_RELU) return MOE_ERR_INVALID;
+  if (p->dtype != MOE_BF16 && p->dtype != MOE_F32) return MOE_ERR_INVALID;
+  if (p->n_bias_sets < 0 || p->n_bias_sets > 2) return MOE_ERR_INVALID;
+  if (!(p->act_clip >= 0.0f)) return MOE_ERR_INVALID;             // rejects NaN
+  if (isnan(p->capacity_factor)) return MOE_ERR_INVALID;
+  if (p->renormalize != 1) return MOE_ERR_UNSUPPORTED;
+  if (p->d_model > (1 << 20) || p->d_expert > (1 << 20)) return MOE_ERR_INVALID;
+  const int64_t rows = p->n_tokens * (p->top_k + p->n_shared);
+  if (rows >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
+  if (p->dtype == MOE_BF16 && ((p->d_model % 8) || (p->d_expert % 8))) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+static inline bool aligned16(const void* q) { return ((uintptr_t)q & 15u) == 0; }
+
+// C = ceil(f * N * k / E) on the exact binary value of f; >= 1 when f > 0;
+// -1 when unlimited.
+static int64_t capacity_of(const moe_problem* p) {
+  const double f = p->capacity_factor;
+  if (!(f > 0.0)) return -1;
+  if (isinf(f)) return -1;
+  const int64_t nk = p->n_tokens * p->top_k;
+  const int64_t E = p->n_experts;
+  if (nk == 0) return 1;
+  int ex = 0;
+  const double fr = frexp(f, &ex);                   // f = fr * 2^ex, fr in [0.5, 1)
+  const int64_t mant = (int64_t)ldexp(fr, 53);       // exact 53-bit integer
+  const int q = ex - 53;                             // f = mant * 2^q
+  __int128 num = (__int128)nk * mant;
+  __int128 den = E;
+  if (q >= 0) {
+    if (q > 40) return INT64_MAX / 2;                 // astronomically large: unlimited in effect
+    num <<= q;
+  } else {
+    if (-q >= 100) return 1;                          // value < 1
+    den <<= -q;
+  }
+  __int128 c = (num + den - 1) / den;
+  if (c < 1) c = 1;
+  if (c > (__int128)(INT64_MAX / 2)) c = INT64_MAX / 2;
+  return (int64_t)c;
+}
+
+static inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+static int run_route(const moe_problem* p, const void* x, const void* w_router,
+                     const float* logit_bias, const float* sel_bias, const uint8_t* modality,
+                     int32_t* idx, float* w, double* z, hipStream_t s) {
+  const int64_t N = p->n_tokens;
+  hipError_t err;
+  if (p->dtype == MOE_BF16)
+    err = launch_router_bf16(static_cast<const uint16_t*>(x),
+                             static_cast<const uint16_t*>(w_router), logit_bias, z, N,
+                             p->d_model, p->n_experts, s);
+  else
+    err = launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
+                            logit_bias, z, N, p->d_model, p->n_experts, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  err = launch_topk(z, p->n_bias_sets ? sel_bias : nullptr, modality, p->n_bias_sets, p->gating,
+                    idx, w, N, p->n_experts, p->top_k, s);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+static int check_route_inputs(const moe_problem* p, const void* x, const void* w_router,
+                              const float* sel_bias, const uint8_t* modality) {
+  if (!x || !w_router) return MOE_ERR_NULL;
+  if (p->n_bias_sets > 0 && !sel_bias) return MOE_ERR_NULL;
+  if (p->n_bias_sets == 2 && !modality) return MOE_ERR_NULL;
+  if (p->dtype == MOE_BF16 && (!aligned16(x) || !aligned16(w_router))) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_workspace_size(const moe_problem* p, size_t* bytes) {
+  const int st = validate(p);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = ws_layout(p).total;
+  return MOE_OK;
+}
+
+int moe_capacity(const moe_problem* p, int64_t* C) {
+  const int st = validate(p);
+  if (st) return st;
+  if (!C) return MOE_ERR_NULL;
+  *C = capacity_of(p);
+  return MOE_OK;
+}
+
+int moe_param_counts(const moe_problem* p, int64_t* expert_total, int64_t* expert_active,
+                     int64_t* router) {
+  const int st = validate(p);
+  if (st) return st;
+  if (!expert_total || !expert_active || !router) return MOE_ERR_NULL;
+  const int64_t m = p->activation == MOE_SWIGLU ? 3 : 2;
+  const int64_t per = m * (int64_t)p->d_model * p->d_expert;
+  *expert_total = (int64_t)(p->n_experts + p->n_shared) * per;
+  *expert_active = (int64_t)(p->top_k + p->n_shared) * per;
+  *router = (int64_t)p->d_model * p->n_experts;
+  return MOE_OK;
+}
+
+int moe_route(const moe_problem* p, const void* x, const void* w_router, const float* logit_bias,
+              const float* sel_bias, const uint8_t* modality, int32_t* topk_idx, float* topk_w,
+              double* logits, void* ws, size_t ws_bytes, void* stream) {
+  int st = validate(p);
+  if (st) return st;
+  if (!topk_idx || !topk_w) return MOE_ERR_NULL;
+  st = check_route_inputs(p, x, w_router, sel_bias, modality);
+  if (st) return st;
+  const size_t need = logits ? 0 : (size_t)p->n_tokens * p->n_experts * 8;
+  if (need && (!ws || ws_bytes < need)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_NULL;
+  if (p->n_tokens == 0) return MOE_OK;
+  double* z = logits ? logits : static_cast<double*>(ws);
+  return run_route(p, x, w_router, logit_bias, sel_bias, modality, topk_idx, topk_w, z, S(stream));
+}
+
+int moe_permute(const moe_problem* p, const int32_t* topk_idx, const uint8_t* modality,
+                int32_t* counts, int32_t* modality_counts, int32_t* offsets, int32_t* row_of,
+                int32_t* token_of_row, uint8_t* drop_mask, void* ws, size_t ws_bytes,
+                void* stream) {
+  const int st = validate(p);
+  if (st) return st;
+  if (!topk_idx || !counts || !offsets || !row_of || !token_of_row || !drop_mask)
+    return MOE_ERR_NULL;
+  if (modality_counts && !modality) return MOE_ERR_NULL;
+  const int64_t N = p->n_tokens;
+  const size_t nk = (size_t)N * p->top_k;
+  const size_t lr_bytes = align256(nk * 4 ? nk * 4 : 1);
+  const size_t need = lr_bytes + (size_t)perm_blocks(N) * 3 * p->n_experts * 4;
+  if (!ws) return MOE_ERR_NULL;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (N == 0) {
+    // nothing routed: zero counts and offsets so the outputs are still defined
+    hipError_t e1 = hipMemsetAsync(counts, 0, (size_t)p->n_experts * 4, S(stream));
+    hipError_t e2 = hipMemsetAsync(offsets, 0, (size_t)(p->n_experts + 1) * 4, S(stream));
+    hipError_t e3 = modality_counts
+                        ? hipMemsetAsync(modality_counts, 0, (size_t)2 * p->n_experts * 4, S(stream))
+                        : hipSuccess;
+    return (e1 || e2 || e3) ? MOE_ERR_HIP : MOE_OK;
+  }
+  char* base = static_cast<char*>(ws);
+  const hipError_t err = launch_permute(
+      topk_idx, modality, counts, modality_counts, offsets, row_of, token_of_row, drop_mask,
+      reinterpret_cast<int32_t*>(base), reinterpret_cast<int32_t*>(base + lr_bytes), N,
+      p->n_experts, p->top_k, capacity_of(p), S(stream));
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_expert_ffn(const moe_problem* p, const void* x, const int32_t* token_of_row,
+                   const int32_t* offsets, const void* w_gate, const void* w_up,
+                   const void* w_down, void* y_rows, void* ws, size_t ws_bytes, void* stream) {
+  const int st = validate(p);
+  if (st) return st;
+  const bool routed = token_of_row != nullptr;
+  if (routed != (offsets != nullptr)) return MOE_ERR_INVALID;
+  if (!x || !w_up || !w_down || !y_rows) return MOE_ERR_NULL;
+  if (p->activation == MOE_SWIGLU && !w_gate) return MOE_ERR_NULL;
+  if (p->dtype == MOE_BF16) {
+    if (!aligned16(x) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(y_rows) ||
+        (w_gate && !aligned16(w_gate)))
+      return MOE_ERR_UNSUPPORTED;
+  }
+  const int64_t N = p->n_tokens;
+  const size_t esz = p->dtype == MOE_BF16 ? 2 : 4;
+  const int E = p->n_experts;
+  const int G = routed ? E : 1;
+  const size_t plan_bytes = align256((size_t)(3 * G + 4) * 4);
+  const size_t rows = routed ? (size_t)N * p->top_k : (size_t)N;
+  const size_t need = plan_bytes + rows * p->d_expert * esz;
+  if (!ws) return MOE_ERR_NULL;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (N == 0) return MOE_OK;
+  char* base = static_cast<char*>(ws);
+  FfnCall c{};
+  c.dtype = p->dtype;
+  c.activation = p->activation;
+  c.clip = p->act_clip;
+  c.N = N;
+  c.d = p->d_model;
+  c.I = p->d_expert;
+  c.x = x;
+  c.plan = reinterpret_cast<int32_t*>(base);
+  c.h = base + plan_bytes;
+  c.y_rows = y_rows;
+  if (routed) {
+    c.n_gather = E;
+    c.routed_rows = N * p->top_k;
+    c.offsets = offsets;
+    c.token_of_row = token_of_row;
+    c.wg = w_gate; c.wu = w_up; c.wd = w_down;
+    c.n_ident = 0;
+    c.identity_row0 = 0;
+    c.max_tiles_m = ffn_max_mtiles(N, p->top_k, E, 0, p->dtype);
+  } else {
+    c.n_gather = 0;
+    c.routed_rows = 0;
+    c.n_ident = 1;
+    c.identity_row0 = 0;
+    c.sg = w_gate; c.su = w_up; c.sd = w_down;
+    c.max_tiles_m = ffn_max_mtiles(N, 0, 0, 1, p->dtype);
+  }
+  return launch_ffn(c, S(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_combine(const moe_problem* p, const void* y_rows, const int32_t* row_of,
+                const float* topk_w, const void* y_shared, void* y, void* stream) {
+  const int st = validate(p);
+  if (st) return st;
+  if (!y_rows || !row_of || !topk_w || !y) return MOE_ERR_NULL;
+  if (p->n_shared > 0 && !y_shared) return MOE_ERR_NULL;
+  if (p->dtype == MOE_BF16 &&
+      (!aligned16(y_rows) || !aligned16(y) || (y_shared && !aligned16(y_shared))))
+    return MOE_ERR_UNSUPPORTED;
+  if (p->n_tokens == 0) return MOE_OK;
+  const hipError_t err = launch_combine(p->dtype, y_rows, row_of, topk_w, y_shared,
+                                        p->n_tokens, p->n_shared, y, p->n_tokens, p->d_model,
+                                        p->top_k, S(stream));
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_forward(const moe_problem* p, const moe_weights* w, const void* x,
+                const float* logit_bias, const float* sel_bias, const uint8_t* modality, void* y,
+                const moe_routing* routing_out, void* ws, size_t ws_bytes, void* stream) {
+  return moe_forward_ex(p, w, x, logit_bias, sel_bias, modality, y, routing_out, nullptr, ws,
+                        ws_bytes, stream);
+}
+
+int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
+                   const float* logit_bias, const float* sel_bias, const uint8_t* modality,
+                   void* y, const moe_routing* routing_out, const moe_profile* prof, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int st = validate(p);
+  if (st) return st;
+  if (!w || !y) return MOE_ERR_NULL;
+  st = check_route_inputs(p, x, w->w_router, sel_bias, modality);
+  if (st) return st;
+  if (!w->w_up || !w->w_down) return MOE_ERR_NULL;
+  if (p->activation == MOE_SWIGLU && !w->w_gate) return MOE_ERR_NULL;
+  if (p->n_shared > 0) {
+    if (!w->ws_up || !w->ws_down) return MOE_ERR_NULL;
+    if (p->activation == MOE_SWIGLU && !w->ws_gate) return MOE_ERR_NULL;
+  }
+  if (p->dtype == MOE_BF16) {
+    const void* ptrs[] = {w->w_gate, w->w_up, w->w_down, w->ws_gate, w->ws_up, w->ws_down, y};
+    for (const void* q : ptrs)
+      if (q && !aligned16(q)) return MOE_ERR_UNSUPPORTED;
+  }
+  if (routing_out && routing_out->modality_counts && !modality) return MOE_ERR_NULL;
+  const WsLayout L = ws_layout(p);
+  if (!ws) return MOE_ERR_NULL;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const int64_t N = p->n_tokens;
+  if (N == 0) return MOE_OK;
+
+  const hipStream_t s = S(stream);
+  char* base = static_cast<char*>(ws);
+  const moe_routing none{};
+  const moe_routing& r = routing_out ? *routing_out : none;
+  double* z = r.logits ? r.logits : reinterpret_cast<double*>(base + L.logits);
+  int32_t* idx = r.topk_idx ? r.topk_idx : reinterpret_cast<int32_t*>(base + L.topk_idx);
+  float* gw = r.topk_w ? r.topk_w : reinterpret_cast<float*>(base + L.topk_w);
+  int32_t* counts = r.counts ? r.counts : reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* offsets = r.offsets ? r.offsets : reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* row_of = r.row_of ? r.row_of : reinterpret_cast<int32_t*>(base + L.row_of);
+  int32_t* tor = r.token_of_row ? r.token_of_row : reinterpret_cast<int32_t*>(base + L.token_of_row);
+  uint8_t* drop = r.drop_mask ? r.drop_mask : reinterpret_cast<uint8_t*>(base + L.drop);
+  int32_t* mcounts = r.modality_counts;
+
+  auto mark = [&](int i) {
+    if (prof && prof->ev[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(prof->ev[i]), s);
+  };
+  mark(2 * MOE_STAGE_ROUTE);
+  st = run_route(p, x, w->w_router, logit_bias, sel_bias, modality, idx, gw, z, s);
+  if (st) return st;
+  mark(2 * MOE_STAGE_ROUTE + 1);
+  mark(2 * MOE_STAGE_PERMUTE);
+  if (launch_permute(idx, modality, counts, mcounts, offsets, row_of, tor, drop,
+                     reinterpret_cast<int32_t*>(base + L.lrank),
+                     reinterpret_cast<int32_t*>(base + L.blk_counts), N, p->n_experts, p->top_k,
+                     capacity_of(p), s) != hipSuccess)
+    return MOE_ERR_HIP;
+  mark(2 * MOE_STAGE_PERMUTE + 1);
+
+  const size_t esz = p->dtype == MOE_BF16 ? 2 : 4;
+  FfnCall c{};
+  c.dtype = p->dtype;
+  c.activation = p->activation;
+  c.clip = p->act_clip;
+  c.N = N;
+  c.d = p->d_model;
+  c.I = p->d_expert;
+  c.n_gather = p->n_experts;
+  c.routed_rows = N * p->top_k;
+  c.offsets = offsets;
+  c.token_of_row = tor;
+  c.n_ident = p->n_shared;
+  c.identity_row0 = N * p->top_k;
+  c.x = x;
+  c.wg = w->w_gate; c.wu = w->w_up; c.wd = w->w_down;
+  c.sg = w->ws_gate; c.su = w->ws_up; c.sd = w->ws_down;
+  c.h = base + L.h;
+  c.y_rows = base + L.yrows;
+  c.plan = reinterpret_cast<int32_t*>(base + L.plan);
+  c.max_tiles_m = ffn_max_mtiles(N, p->top_k, p->n_experts, p->n_shared, p->dtype);
+  if (prof) {
+    for (int i = 0; i < 6; ++i) c.marks[i] = prof->ev[2 * MOE_STAGE_PLAN + i];
+  }
+  if (launch_ffn(c, s) != hipSuccess) return MOE_ERR_HIP;
+
+  const void* y_shared = p->n_shared ? static_cast<const void*>(base + L.yrows +
+                                                                (size_t)N * p->top_k * p->d_model * esz)
+                                     : nullptr;
+  mark(2 * MOE_STAGE_COMBINE);
+  if (launch_combine(p->dtype, base + L.yrows, row_of, gw, y_shared, N, p->n_shared, y, N,
+                     p->d_model, p->top_k, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  mark(2 * MOE_STAGE_COMBINE + 1);
+  return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_INVALID: return "a size or option is out of range";
+    case MOE_ERR_UNSUPPORTED: return "unsupported (alignment or option)";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_version(void) { return "0.1.0 gfx950"; }
+
+}  // extern "C"

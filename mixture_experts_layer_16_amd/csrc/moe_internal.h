@@ -1,0 +1,169 @@
+// Internal declarations shared by the HIP sources of the MoE-layer library.
+// Nothing here is part of the public ABI (include/moe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// tiling constants shared by the host planner and the kernels
+
+constexpr int kGemmBM = 128;       // rows (tokens) per grouped-GEMM tile
+constexpr int kGemmBN = 256;       // weight rows per tile (gate+up: 128 + 128)
+constexpr int kGemmBK = 64;        // reduction slice staged in LDS
+constexpr int kF32BM = 64;         // fp32 path tile
+constexpr int kF32BN = 64;
+constexpr int kPermTokens = 256;   // tokens per block of the rank kernel
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxShared = 8;
+constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, one L2 each
+
+// ---------------------------------------------------------------------------
+// device workspace layout (byte offsets from the workspace base)
+
+struct WsLayout {
+  size_t logits;        // f64 [N][E]
+  size_t topk_idx;      // i32 [N*k]
+  size_t topk_w;        // f32 [N*k]
+  size_t counts;        // i32 [E]
+  size_t mod_counts;    // i32 [2][E]
+  size_t offsets;       // i32 [E+1]
+  size_t row_of;        // i32 [N*k]
+  size_t token_of_row;  // i32 [N*k]
+  size_t drop;          // u8  [N*k]
+  size_t lrank;         // i32 [N*k]   block-local ranks
+  size_t blk_counts;    // i32 [nblk][E] per-block demand, then per-block bases
+  size_t plan;          // i32 [3*G+1] tile plan of the grouped GEMMs
+  size_t h;             // act [N*k + N*S][I]   expert hidden activations
+  size_t yrows;         // act [N*k + N*S][d]   expert outputs per row
+  size_t total;
+};
+
+WsLayout ws_layout(const moe_problem* p);
+int64_t perm_blocks(int64_t N);
+
+// plan layout: tile_start[G+1], row_begin[G], rows[G]
+struct PlanView {
+  int32_t* tile_start;
+  int32_t* row_begin;
+  int32_t* rows;
+};
+inline PlanView plan_view(int32_t* plan, int G) {
+  return PlanView{plan, plan + (G + 1), plan + (G + 1) + G};
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each enqueues on `stream`, returns hipError_t of the launch)
+
+hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* w, const float* logit_bias,
+                              double* z, int64_t N, int d, int E, hipStream_t s);
+hipError_t launch_router_f32(const float* x, const float* w, const float* logit_bias,
+                             double* z, int64_t N, int d, int E, hipStream_t s);
+hipError_t launch_topk(const double* z, const float* sel_bias, const uint8_t* modality,
+                       int n_bias_sets, int gating, int32_t* idx, float* w, int64_t N,
+                       int E, int k, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* idx, const uint8_t* modality, int32_t* counts,
+                          int32_t* mod_counts, int32_t* offsets, int32_t* row_of,
+                          int32_t* token_of_row, uint8_t* drop, int32_t* lrank,
+                          int32_t* blk_counts, int64_t N, int E, int k, int64_t C,
+                          hipStream_t s);
+
+// Grouped FFN over G groups.  Groups [0, n_gather) are routed experts whose
+// rows come from `offsets` (row r of group g is x[token_of_row[offsets[g]+r]]);
+// the remaining groups are dense over all N tokens, one per "identity" weight
+// set, writing rows [identity_row0 + i*N, ...).
+struct FfnCall {
+  int dtype;                   // MOE_BF16 / MOE_F32
+  int activation;              // MOE_SWIGLU / MOE_RELU
+  float clip;
+  int64_t N;                   // tokens
+  int d, I;
+  int n_gather;                // routed groups (0 for the dense-only call)
+  int64_t routed_rows;         // N*k: rows available to the routed groups
+  const int32_t* offsets;      // [n_gather+1] device, or NULL
+  const int32_t* token_of_row; // device, or NULL
+  int n_ident;                 // dense groups
+  int64_t identity_row0;       // first row of the dense groups in h / y_rows
+  const void* x;
+  const void *wg, *wu, *wd;    // routed weights ([n_gather][..])
+  const void *sg, *su, *sd;    // dense-group weights ([n_ident][..])
+  void* h;                     // [rows][I]
+  void* y_rows;                // [rows][d]
+  int32_t* plan;               // workspace for the tile plan
+  int64_t max_tiles_m;         // host upper bound on m-tiles (grid sizing)
+  void* marks[6];              // optional hipEvent_t: before/after plan, gate/up, down
+};
+hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
+int64_t ffn_max_mtiles(int64_t N, int k, int E, int S, int dtype);
+
+hipError_t launch_combine(int dtype, const void* y_rows, const int32_t* row_of,
+                          const float* topk_w, const void* y_shared, int64_t shared_stride_rows,
+                          int S, void* y, int64_t N, int d, int k, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// round to nearest, ties to even
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp32 -> fp16 bits, round to nearest even, saturating at +-65504
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
+  f = fminf(fmaxf(f, -65504.0f), 65504.0f);
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+// two packed bf16 -> two packed fp16.  Exact for values in fp16's normal range
+// (bf16's 8-bit significand fits in fp16's 11 bits); smaller magnitudes are
+// truncated to the fp16 subnormal grid (error < 2^-24); larger ones saturate.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const float lo = __uint_as_float(w << 16);
+  const float hi = __uint_as_float(w & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// Exclusive scan of n (<= 2 * blockDim) ints held in LDS `v`; returns the total.
+// blockDim.x must be 1024.
+__device__ inline int block_exclusive_scan_1024(int32_t* v, int n, int32_t* tmp) {
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int lo = tid * per;
+  int s = 0;
+  for (int i = 0; i < per; ++i)
+    if (lo + i < n) s += v[lo + i];
+  tmp[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = (tid >= off) ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  const int total = tmp[1023];
+  int run = tmp[tid] - s;   // exclusive prefix of this thread's chunk
+  for (int i = 0; i < per; ++i)
+    if (lo + i < n) {
+      const int x = v[lo + i];
+      v[lo + i] = run;
+      run += x;
+    }
+  __syncthreads();
+  return total;
+}
+
+}  // namespace moe

@@ -1,0 +1,176 @@
+// Dispatch: per-expert histogram, capacity, token-order ranks and the slot
+// permutation.
+//
+// The capacity rule and the slot order are those of "Mixture-of-Experts :
+// routage et capacité" (cours.spawnkit.ai), sections "L'idée — Capacité" and
+// "Cas guidé — trace complète": tokens arrive in batch order, expert e keeps its
+// first C arrivals (C = ceil(N*k/E * f)) and drops the rest; kept assignments
+// are packed expert by expert, in arrival order.
+//
+// Ranks must follow token order, so they are not taken from atomics (whose
+// order follows the hardware).  Three passes:
+//   1. rank:    per block of 256 tokens, each wave ranks its 64 tokens' k
+//               assignments with ballot-built peer masks (lanes holding the same
+//               expert), keeps per-wave running counts in LDS, then turns them
+//               into block-local ranks and a per-block histogram (also split by
+//               modality);
+//   2. scan:    per expert, an exclusive scan of the block histograms gives each
+//               block's base rank and the expert's demand; kept = min(demand, C);
+//               an exclusive scan over experts gives the offsets;
+//   3. scatter: rank = block base + local rank; kept iff rank < C.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int PR_WAVES = kPermTokens / 64;   // 4 waves, 64 tokens each
+
+__device__ __forceinline__ int expert_bits(int E) {
+  int b = 1;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+// stride of one block's histogram record: [3][E] (all, text, image)
+__global__ __launch_bounds__(256) void perm_rank_kernel(
+    const int32_t* __restrict__ idx, const uint8_t* __restrict__ modality,
+    int32_t* __restrict__ lrank, int32_t* __restrict__ blk, int64_t N, int E, int k) {
+  extern __shared__ int32_t lds[];                // cnt[4][E], then mcnt[2][E]
+  int32_t* cnt = lds;
+  int32_t* mcnt = lds + PR_WAVES * E;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < (PR_WAVES + 2) * E; i += blockDim.x) lds[i] = 0;
+  __syncthreads();
+
+  const int64_t NK = N * k;
+  const int64_t a_wave = ((int64_t)blockIdx.x * kPermTokens + 64 * wave) * k;
+  const int nbits = expert_bits(E);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t* wcnt = cnt + wave * E;
+
+  for (int c = 0; c < k; ++c) {
+    const int64_t a = a_wave + (int64_t)c * 64 + lane;
+    int e = -1;
+    if (a < NK) e = idx[a];
+    const bool valid = (e >= 0) && (e < E);
+    uint64_t peers = __ballot(valid);
+#pragma unroll 1
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = valid && ((e >> bit) & 1);
+      const uint64_t m = __ballot(on);
+      peers &= on ? m : ~m;
+    }
+    if (valid) {
+      const int before = __popcll(peers & lt_mask);
+      const int old = wcnt[e];
+      if (before == 0) wcnt[e] = old + __popcll(peers);   // the group's lowest lane
+      lrank[a] = old + before;
+      if (modality) atomicAdd(&mcnt[(modality[a / k] ? 1 : 0) * E + e], 1);
+    }
+  }
+  __syncthreads();
+
+  int32_t* rec = blk + (int64_t)blockIdx.x * 3 * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < PR_WAVES; ++w) {
+      const int v = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += v;
+    }
+    rec[e] = run;
+    rec[E + e] = mcnt[e];
+    rec[2 * E + e] = mcnt[E + e];
+  }
+  __syncthreads();
+
+  for (int c = 0; c < k; ++c) {
+    const int64_t a = a_wave + (int64_t)c * 64 + lane;
+    if (a >= NK) break;
+    const int e = idx[a];
+    if (e >= 0 && e < E) lrank[a] += wcnt[e];
+  }
+}
+
+__global__ __launch_bounds__(1024) void perm_scan_kernel(
+    int32_t* __restrict__ blk, int nblk, int32_t* __restrict__ counts,
+    int32_t* __restrict__ mod_counts, int32_t* __restrict__ offsets, int E, int64_t C) {
+  __shared__ int32_t kept[kMaxExperts];
+  __shared__ int32_t tmp[1024];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0, m0 = 0, m1 = 0;
+    for (int b = 0; b < nblk; ++b) {
+      int32_t* rec = blk + (int64_t)b * 3 * E;
+      const int v = rec[e];
+      rec[e] = run;
+      run += v;
+      m0 += rec[E + e];
+      m1 += rec[2 * E + e];
+    }
+    counts[e] = run;
+    if (mod_counts) {
+      mod_counts[e] = m0;
+      mod_counts[E + e] = m1;
+    }
+    kept[e] = (C < 0 || run < C) ? run : (int)C;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan_1024(kept, E, tmp);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = kept[e];
+  if (threadIdx.x == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ lrank,
+    const int32_t* __restrict__ blk, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ token_of_row,
+    uint8_t* __restrict__ drop, int64_t N, int E, int k, int64_t C) {
+  const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (a >= N * k) return;
+  const int e = idx[a];
+  if (e < 0 || e >= E) {
+    row_of[a] = -1;
+    drop[a] = 1;
+    return;
+  }
+  const int64_t t = a / k;
+  const int64_t b = t / kPermTokens;
+  const int64_t r = (int64_t)blk[b * 3 * E + e] + lrank[a];
+  if (C < 0 || r < C) {
+    const int row = offsets[e] + (int)r;
+    row_of[a] = row;
+    token_of_row[row] = (int32_t)t;
+    drop[a] = 0;
+  } else {
+    row_of[a] = -1;
+    drop[a] = 1;
+  }
+}
+
+}  // namespace
+
+int64_t perm_blocks(int64_t N) { return (N + kPermTokens - 1) / kPermTokens; }
+
+hipError_t launch_permute(const int32_t* idx, const uint8_t* modality, int32_t* counts,
+                          int32_t* mod_counts, int32_t* offsets, int32_t* row_of,
+                          int32_t* token_of_row, uint8_t* drop, int32_t* lrank,
+                          int32_t* blk_counts, int64_t N, int E, int k, int64_t C,
+                          hipStream_t s) {
+  const int64_t nblk = perm_blocks(N);
+  const size_t lds = (size_t)(PR_WAVES + 2) * E * sizeof(int32_t);
+  perm_rank_kernel<<<(unsigned)nblk, 256, lds, s>>>(idx, mod_counts ? modality : nullptr,
+                                                     lrank, blk_counts, N, E, k);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  perm_scan_kernel<<<1, 1024, 0, s>>>(blk_counts, (int)nblk, counts, mod_counts, offsets, E, C);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t nk = N * k;
+  perm_scatter_kernel<<<(unsigned)((nk + 255) / 256), 256, 0, s>>>(
+      idx, lrank, blk_counts, offsets, row_of, token_of_row, drop, N, E, k, C);
+  return hipGetLastError();
+}
+
+}  // namespace moe

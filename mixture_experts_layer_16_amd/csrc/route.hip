@@ -1,0 +1,223 @@
+// Router projection, scoring, selection keys, top-k and gate weights.
+//
+// Steps 1-3 of "Основы MoE" (ai.flicky.cc), section "Как устроен MoE-слой":
+// logits z = x W_g, scores softmax(z) (or the sigmoid of the DeepSeek-V3
+// variant mentioned in the same section), the k largest, renormalised weights.
+// Selection bias moves only the choice ("Le groupe d'experts (MoE)", section
+// "Étape 1: le routeur"; V4.1 page, "L'équilibrage de charge"), one bias set per
+// modality (V4.1 page, "La nouveauté de V4.1").
+#include "moe_internal.h"
+
+#include <math.h>
+
+namespace moe {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+// ---------------------------------------------------------------------------
+// bf16 router logits on the matrix cores.
+//
+// Each v_mfma_f32_16x16x32_bf16 sums 32 exact bf16 x bf16 products into a
+// fresh fp32 partial; the partial is then added into a float64 accumulator.
+// The fp32 rounding error is therefore confined to 32-term partial sums and the
+// logits come out within ~1e-7 of their scale of the exact dot product, which
+// keeps the top-k decision equal to the float64 one except for near-ties.
+//
+// Block: 4 waves; tile 64 tokens x 64 experts; wave w owns 16 tokens and the
+// 64 experts (four 16x16 output tiles).  Operands are read straight from global
+// memory (x rows are read once per expert tile, the router matrix stays in L2).
+constexpr int RT_TOK = 64;
+constexpr int RT_EXP = 64;
+
+__global__ __launch_bounds__(256) void router_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const float* __restrict__ logit_bias, double* __restrict__ z, int64_t N, int d, int E) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t tok0 = (int64_t)blockIdx.x * RT_TOK + wave * 16;
+  const int e0 = blockIdx.y * RT_EXP;
+  const int r16 = lane & 15;     // A row / B column supplied by this lane
+  const int kq = lane >> 4;      // which 8-wide k chunk of the 32-wide step
+
+  int64_t arow = tok0 + r16;
+  if (arow >= N) arow = N - 1;
+  const uint16_t* ap = x + arow * (int64_t)d + kq * 8;
+  const uint16_t* bp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int e = e0 + 16 * j + r16;
+    if (e >= E) e = E - 1;
+    bp[j] = w + (int64_t)e * d + kq * 8;
+  }
+
+  double acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[j][v] = 0.0;
+
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < d; k0 += 32) {
+    const bool ok = (k0 + kq * 8) < d;
+    u32x4_t a = {0u, 0u, 0u, 0u};
+    u32x4_t b[4];
+    if (ok) a = *reinterpret_cast<const u32x4_t*>(ap + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b[j] = (u32x4_t){0u, 0u, 0u, 0u};
+      if (ok) b[j] = *reinterpret_cast<const u32x4_t*>(bp[j] + k0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[j]), zero4, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[j][v] += (double)p[v];
+    }
+  }
+
+  // D layout of the 16x16 output: lane holds column (lane & 15), rows 4*(lane>>4)+v
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + 16 * j + r16;
+    if (e >= E) continue;
+    const double ob = logit_bias ? (double)logit_bias[e] : 0.0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t t = tok0 + 4 * kq + v;
+      if (t < N) z[t * E + e] = acc[j][v] + ob;
+    }
+  }
+}
+
+// fp32 inputs: products of two floats are exact in float64, so the float64
+// FMA chain gives the logits to float64 accuracy.
+__global__ __launch_bounds__(256) void router_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w,
+    const float* __restrict__ logit_bias, double* __restrict__ z, int64_t N, int d, int E) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N * E) return;
+  const int64_t t = i / E;
+  const int e = (int)(i - t * E);
+  const float* xr = x + t * d;
+  const float* wr = w + (int64_t)e * d;
+  double s = 0.0;
+  for (int c = 0; c < d; ++c) s = fma((double)xr[c], (double)wr[c], s);
+  if (logit_bias) s += (double)logit_bias[e];
+  z[i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// top-k: one token per wavefront.  Lane l owns experts l, l+64, l+128, ...
+// Each of the k rounds is a 64-lane argmax on (key desc, index asc) by xor
+// butterflies; lane r keeps the r-th winner.  Keys and scores are float64.
+constexpr int TK_MAXJ = kMaxExperts / 64;
+
+__device__ __forceinline__ bool better(double ka, int ea, double kb, int eb) {
+  return ka > kb || (ka == kb && ea < eb);
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(
+    const double* __restrict__ z, const float* __restrict__ sel_bias,
+    const uint8_t* __restrict__ modality, int n_bias_sets, int gating,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_w, int64_t N, int E, int k) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;
+  const double* zr = z + t * E;
+  const int m = (n_bias_sets == 2) ? (int)modality[t] : 0;
+  const float* bias = n_bias_sets ? sel_bias + (int64_t)m * E : nullptr;
+  const bool sig = (gating == MOE_SIGMOID);
+
+  double key[TK_MAXJ], sc[TK_MAXJ];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int j = 0; j < TK_MAXJ; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = -INFINITY;
+    sc[j] = 0.0;
+    if (e < E) {
+      const double zz = zr[e];
+      const double s = sig ? 1.0 / (1.0 + exp(-zz)) : zz;   // sigmoid score, or the logit
+      double kk = s;
+      if (bias) kk += (double)bias[e];
+      key[j] = kk;
+      sc[j] = s;
+      valid |= 1u << j;
+    }
+  }
+
+  int my_e = 0;          // lane r < k: expert of round r
+  double my_s = 0.0;     // its logit (softmax) or sigmoid score
+  for (int r = 0; r < k; ++r) {
+    double bk = -INFINITY, bs = 0.0;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < TK_MAXJ; ++j) {
+      if (valid & (1u << j)) {
+        const int e = lane + 64 * j;
+        if (better(key[j], e, bk, be)) { bk = key[j]; be = e; bs = sc[j]; }
+      }
+    }
+    const double own_s = bs;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ok = __shfl_xor(bk, off);
+      const int oe = __shfl_xor(be, off);
+      if (better(ok, oe, bk, be)) { bk = ok; be = oe; }
+    }
+    const int owner = be & 63;
+    const double ws = __shfl(own_s, owner);
+    if (lane == owner) valid &= ~(1u << (be >> 6));
+    if (lane == r) { my_e = be; my_s = ws; }
+  }
+
+  // gate weights over the chosen k: softmax over the chosen logits (equal to the
+  // renormalised full softmax), or sigmoid scores divided by their sum.
+  const bool mine = lane < k;
+  double g;
+  if (!sig) {
+    double mx = mine ? my_s : -INFINITY;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+    g = mine ? exp(my_s - mx) : 0.0;
+  } else {
+    g = mine ? my_s : 0.0;
+  }
+  double sum = g;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (mine) {
+    out_idx[t * k + lane] = my_e;
+    out_w[t * k + lane] = (float)(g / sum);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* w, const float* logit_bias,
+                              double* z, int64_t N, int d, int E, hipStream_t s) {
+  dim3 grid((unsigned)((N + RT_TOK - 1) / RT_TOK), (unsigned)((E + RT_EXP - 1) / RT_EXP));
+  router_bf16_kernel<<<grid, 256, 0, s>>>(x, w, logit_bias, z, N, d, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_f32(const float* x, const float* w, const float* logit_bias,
+                             double* z, int64_t N, int d, int E, hipStream_t s) {
+  const int64_t n = N * E;
+  router_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, w, logit_bias, z, N, d, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const double* z, const float* sel_bias, const uint8_t* modality,
+                       int n_bias_sets, int gating, int32_t* idx, float* w, int64_t N,
+                       int E, int k, hipStream_t s) {
+  topk_kernel<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(z, sel_bias, modality, n_bias_sets,
+                                                       gating, idx, w, N, E, k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -57,13 +57,14 @@ class Workload:
     decode: bool = False         # decode token stream (same weights as prefill)
     seed: int = 0
     w_std: float = 0.02
+    toy_draws: bool = False      # reproduce the NumPy fiche's draw order (toy layer)
     notes: str = ""
 
 
 # The named workloads.  Sizes are the ones the MoE-layer descriptions give.
 WORKLOADS = {
     "toy": Workload("toy", N=1000, d=64, E=8, k=2, I=256, S=0, gating="softmax",
-                    activation="relu", dtype="f32", seed=42, w_std=0.1,
+                    activation="relu", dtype="f32", seed=42, w_std=0.1, toy_draws=True,
                     notes="NumPy MoE fiche toy: 8 two-layer ReLU experts, top-2"),
     "cap": Workload("cap", N=16384, d=2048, E=64, k=2, I=1408, S=1, f=1.0,
                     gating="softmax", zipf_offset=1.1, seed=1,
@@ -154,6 +155,8 @@ def modality_flags(w: Workload) -> Optional[np.ndarray]:
     of floor(image_frac * segment) tokens at a seeded start."""
     if w.n_bias_sets != 2:
         return None
+    if w.N == 0:
+        return np.zeros(0, dtype=np.uint8)
     seg = min(2048, w.N)
     nseg = max(1, w.N // seg)
     flags = np.zeros(w.N, dtype=np.uint8)
@@ -172,7 +175,7 @@ def modality_flags(w: Workload) -> Optional[np.ndarray]:
 
 def tokens(w: Workload) -> np.ndarray:
     """x [N, d], encoded (bf16 bits or float32)."""
-    if w.name.startswith("toy"):
+    if w.toy_draws:
         return _toy_draws(w)["tokens"]
     t_id = T_X_DECODE if w.decode else T_X
     x = _normal(_rng(w.seed, t_id), (w.N, w.d), 0.0, 1.0)
@@ -186,7 +189,7 @@ def tokens(w: Workload) -> np.ndarray:
 
 def router(w: Workload) -> np.ndarray:
     """Router weights in the library layout [E][d] (row e scores expert e)."""
-    if w.name.startswith("toy"):
+    if w.toy_draws:
         return _toy_draws(w)["router"]
     return _encode(w, _normal(_rng(w.seed, T_ROUTER), (w.E, w.d), 0.0, w.w_std))
 
@@ -210,7 +213,7 @@ def selection_bias(w: Workload) -> Optional[np.ndarray]:
 def expert_weights(w: Workload, e: int, shared: bool = False):
     """(w_gate [I][d] or None, w_up [I][d], w_down [d][I]) for routed expert e or
     shared expert e, encoded.  For ReLU experts w_up = W1^T and w_down = W2^T."""
-    if w.name.startswith("toy"):
+    if w.toy_draws:
         t = _toy_draws(w)
         return None, t["w_up"][e], t["w_down"][e]
     tg, tu, td = (T_SGATE, T_SUP, T_SDOWN) if shared else (T_WGATE, T_WUP, T_WDOWN)

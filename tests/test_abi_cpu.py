@@ -1,0 +1,165 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every function
+the header declares, and its host-side logic (validation, exact capacity,
+parameter counts, workspace sizing) is right.  No kernel is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIBSO = os.path.join(ROOT, "mixture_experts_layer_16_amd", "libmoe.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIBSO), reason="libmoe.so not built")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mixture_experts_layer_16_amd import _lib
+    return _lib
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return set(re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", txt, flags=re.M))
+
+
+def test_header_and_exports_agree(L):
+    decl = header_functions()
+    assert decl == set(L.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", LIBSO], capture_output=True,
+                         text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = decl - syms
+    assert not missing, f"declared but not exported: {missing}"
+    for name in decl:
+        assert hasattr(L.LIB, name)
+
+
+def test_version_and_status_strings(L):
+    assert "gfx950" in L.moe_version()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.moe_status_string(code) != "unknown status"
+    assert L.moe_status_string(7) == "unknown status"
+
+
+TRACE = [  # routing slides' trace and its variants: (N, k, E, f, C)
+    (8, 2, 4, 1.25, 5), (8, 2, 4, 1.0, 4), (8, 2, 4, 2.0, 8), (8, 2, 4, 1.5, 6), (8, 1, 4, 1.25, 3),
+]
+
+
+@pytest.mark.parametrize("N,k,E,f,C", TRACE)
+def test_capacity_printed_values(L, N, k, E, f, C):
+    p = L.problem(N, 8, E, k, 8, capacity_factor=f)
+    assert L.moe_capacity(p) == C
+
+
+def test_capacity_matches_oracle_exactly(L):
+    rng = np.random.default_rng(0)
+    p = L.problem(16384, 2048, 64, 2, 1408, capacity_factor=1.0)
+    assert L.moe_capacity(p) == 512
+    assert L.moe_capacity(L.problem(16, 8, 4, 2, 8, capacity_factor=0.0)) == -1
+    assert L.moe_capacity(L.problem(16, 8, 4, 2, 8, capacity_factor=-1.0)) == -1
+    for _ in range(300):
+        N = int(rng.integers(0, 50000))
+        E = int(rng.integers(1, 1025))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        f = float(rng.choice([rng.random() * 3, 0.1, 1 / 3, 1.25, 1e-9, 7.0]))
+        got = L.moe_capacity(L.problem(N, 8, E, k, 8, capacity_factor=f))
+        want = O.capacity(f, N, k, E)
+        assert got == (want if N else 1), (N, E, k, f)
+
+
+def test_param_counts_match_closed_forms(L):
+    cases = [(64, 256, 8, 2, 0, "relu"), (7168, 2048, 256, 8, 1, "swiglu"),
+             (5120, 2304, 384, 6, 1, "swiglu"), (2048, 1408, 64, 2, 1, "swiglu")]
+    for d, I, E, k, S, act in cases:
+        p = L.problem(1, d, E, k, I, S=S, activation=act, dtype="f32" if act == "relu" else "bf16")
+        assert L.moe_param_counts(p) == O.layer_params(d, I, E, k, S, act)
+    # the fiche's toy printout and DeepSeek-V3's per-expert size
+    p = L.problem(1000, 64, 8, 2, 256, activation="relu", dtype="f32")
+    assert L.moe_param_counts(p)[:2] == (262144, 65536)
+
+
+def test_workspace_size_grows_with_tokens(L):
+    a = L.moe_workspace_size(L.problem(100, 256, 8, 2, 256, S=1))
+    b = L.moe_workspace_size(L.problem(1000, 256, 8, 2, 256, S=1))
+    assert 0 < a < b
+    # holds the routed + shared hidden rows and output rows at least
+    N, d, E, k, I, S = 1000, 256, 8, 2, 256, 1
+    assert b >= (N * k + N * S) * (d + I) * 2
+
+
+BAD = [  # (overrides, expected status)
+    (dict(k=0), -2), (dict(k=9), -2), (dict(E=0), -2), (dict(E=2000, k=2), -2),
+    (dict(N=-1), -2), (dict(d=0), -2), (dict(I=0), -2), (dict(S=-1), -2), (dict(S=9), -2),
+    (dict(gating=5), -2), (dict(activation=3), -2), (dict(dtype=4), -2), (dict(n_bias_sets=3), -2),
+    (dict(act_clip=float("nan")), -2), (dict(capacity_factor=float("nan")), -2),
+    (dict(d=100), -3), (dict(I=36), -3), (dict(renormalize=0), -3), (dict(k=33, E=64), -2),
+]
+
+
+@pytest.mark.parametrize("over,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_validation_codes(L, over, code):
+    base = dict(N=64, d=128, E=8, k=2, I=64, S=1, gating=0, activation=0, dtype=0, n_bias_sets=0,
+                act_clip=0.0, capacity_factor=0.0, renormalize=1)
+    base.update(over)
+    p = L.Problem(base["N"], base["d"], base["E"], base["k"], base["I"], base["S"],
+                  base["gating"], base["activation"], base["dtype"], base["n_bias_sets"],
+                  base["renormalize"], base["act_clip"], base["capacity_factor"])
+    out = ctypes.c_size_t()
+    assert L.LIB.moe_workspace_size(ctypes.byref(p), ctypes.byref(out)) == code
+
+
+def test_device_entry_points_reject_before_launch(L):
+    """Argument errors are reported on the host, before anything is launched
+    (no GPU is touched: the fake addresses below are never dereferenced)."""
+    fake = 0x10000   # 16-byte aligned, never used
+    p = L.problem(64, 128, 8, 2, 64, S=1)
+    lib = L.LIB
+    # NULL x
+    assert lib.moe_route(ctypes.byref(p), None, fake, None, None, None, fake, fake, fake, None, 0,
+                         None) == -1
+    # logits NULL and no workspace -> NULL workspace; too small -> -4
+    assert lib.moe_route(ctypes.byref(p), fake, fake, None, None, None, fake, fake, None, None, 0,
+                         None) == -1
+    assert lib.moe_route(ctypes.byref(p), fake, fake, None, None, None, fake, fake, None, fake, 8,
+                         None) == -4
+    # misaligned bf16 operand
+    assert lib.moe_route(ctypes.byref(p), fake + 2, fake, None, None, None, fake, fake, fake, None,
+                         0, None) == -3
+    # two bias sets need the modality flags; one set needs the bias
+    p2 = L.problem(64, 128, 8, 2, 64, gating="sigmoid", n_bias_sets=2)
+    assert lib.moe_route(ctypes.byref(p2), fake, fake, None, fake, None, fake, fake, fake, None, 0,
+                         None) == -1
+    p1 = L.problem(64, 128, 8, 2, 64, gating="sigmoid", n_bias_sets=1)
+    assert lib.moe_route(ctypes.byref(p1), fake, fake, None, None, None, fake, fake, fake, None, 0,
+                         None) == -1
+    # permute: missing outputs, too-small workspace
+    assert lib.moe_permute(ctypes.byref(p), fake, None, None, None, fake, fake, fake, fake, fake,
+                           1 << 20, None) == -1
+    assert lib.moe_permute(ctypes.byref(p), fake, None, fake, None, fake, fake, fake, fake, fake, 4,
+                           None) == -4
+    # expert ffn: token_of_row without offsets is inconsistent
+    assert lib.moe_expert_ffn(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake, fake,
+                              1 << 30, None) == -2
+    # SwiGLU needs the gate matrix
+    assert lib.moe_expert_ffn(ctypes.byref(p), fake, None, None, None, fake, fake, fake, fake,
+                              1 << 30, None) == -1
+    # combine with shared experts needs y_shared
+    assert lib.moe_combine(ctypes.byref(p), fake, fake, fake, None, fake, None) == -1
+    # forward: NULL weights struct, too-small workspace
+    assert lib.moe_forward(ctypes.byref(p), None, fake, None, None, None, fake, None, fake, 1 << 30,
+                           None) == -1
+    w = L.Weights(fake, fake, fake, fake, fake, fake, fake)
+    assert lib.moe_forward(ctypes.byref(p), ctypes.byref(w), fake, None, None, None, fake, None,
+                           fake, 16, None) == -4
+    ws_shared_missing = L.Weights(fake, fake, fake, fake, None, None, None)
+    assert lib.moe_forward(ctypes.byref(p), ctypes.byref(ws_shared_missing), fake, None, None,
+                           None, fake, None, fake, 1 << 40, None) == -1

@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--workload", default="cap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the run, copy 256 MiB device-to-device once: a kernel of known "
+                         "traffic to scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -243,6 +246,14 @@ def main():
     roof["kernel"] = kname
     roof["ms_per_launch"] = gu_ms
     roof["algorithmic_per_launch"] = gu_bytes if decode else gu_flops
+
+    if args.calibrate_copy:
+        a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy of 256 MiB done")
 
     cpu = None
     if not args.no_cpu_baseline:

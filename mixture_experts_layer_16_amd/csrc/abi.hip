@@ -246,14 +246,12 @@ int moe_expert_ffn(const moe_problem* p, const void* x, const int32_t* token_of_
     c.wg = w_gate; c.wu = w_up; c.wd = w_down;
     c.n_ident = 0;
     c.identity_row0 = 0;
-    c.max_tiles_m = ffn_max_mtiles(N, p->top_k, E, 0, p->dtype);
   } else {
     c.n_gather = 0;
     c.routed_rows = 0;
     c.n_ident = 1;
     c.identity_row0 = 0;
     c.sg = w_gate; c.su = w_up; c.sd = w_down;
-    c.max_tiles_m = ffn_max_mtiles(N, 0, 0, 1, p->dtype);
   }
   return launch_ffn(c, S(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -357,7 +355,6 @@ int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
   c.h = base + L.h;
   c.y_rows = base + L.yrows;
   c.plan = reinterpret_cast<int32_t*>(base + L.plan);
-  c.max_tiles_m = ffn_max_mtiles(N, p->top_k, p->n_experts, p->n_shared, p->dtype);
   if (prof) {
     for (int i = 0; i < 6; ++i) c.marks[i] = prof->ev[2 * MOE_STAGE_PLAN + i];
   }

@@ -23,6 +23,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
 enum { MODE_GATEUP = 0, MODE_RELU_UP = 1, MODE_DOWN = 2 };
 
+
+
 // ---------------------------------------------------------------------------
 // tile plan: groups [0, n_gather) from offsets, then n_ident dense groups.
 
@@ -65,10 +67,11 @@ struct Tile {
   bool ok;
 };
 
-// Block -> tile.  Tiles are ordered (group, n-tile, m-tile) so the m-tiles that
-// share one weight slab are consecutive; consecutive tiles go to the same XCD
-// (blocks are dealt to the 8 XCDs round-robin), so a slab is fetched into that
-// XCD's L2 once and reused by its m-tiles.
+// Block -> tile.  Consecutive tile indices go to the same XCD (blocks are dealt
+// to the 8 XCDs round-robin, so block b maps to index (b % 8) * per + b / 8);
+// within a group, tiles are ordered by super-rows of a few m-tiles, n-tile
+// major inside each, so the tiles one XCD runs together share weight rows and
+// token rows in that XCD's L2.
 __device__ __forceinline__ Tile decode_tile(const int32_t* __restrict__ plan, int G, int ntn,
                                             int BM, int CT) {
   Tile t;
@@ -88,8 +91,14 @@ __device__ __forceinline__ Tile decode_tile(const int32_t* __restrict__ plan, in
   const int g = lo;
   const int mtg = tile_start[g + 1] - tile_start[g];
   const int local = L - tile_start[g] * ntn;
-  const int nt = local / mtg;
-  const int mtile = local - nt * mtg;
+  // within a group: super-rows of GM m-tiles; inside one, n-tile major, m-tile
+  // minor, so the tiles in flight on one XCD share both x rows and weight rows
+  const int GM = BM >= 256 ? 4 : 8;
+  const int sr = local / (GM * ntn);
+  const int rem = local - sr * GM * ntn;
+  const int gm = min(GM, mtg - sr * GM);
+  const int nt = rem / gm;
+  const int mtile = sr * GM + (rem - nt * gm);
   t.g = g;
   t.m0 = mtile * BM;
   t.n0 = nt * CT;
@@ -97,6 +106,17 @@ __device__ __forceinline__ Tile decode_tile(const int32_t* __restrict__ plan, in
   t.rb = plan[G + 1 + g];
   t.ok = true;
   return t;
+}
+
+// LDS line swizzle: XOR applied to the 16-byte chunk position inside a
+// 128-byte line.  Chosen so that any 8 consecutive rows, and the rows of each
+// parity among any 16 consecutive rows, use distinct positions: conflict-free
+// whether the LDS serves a 128-bit read 8 lanes (32 banks) or 16 lanes (64
+// banks) at a time.  RPL = rows per line (1 for 64-wide k-slices, 2 for 32).
+template <int RPL>
+__device__ __forceinline__ int lds_swizzle(int line) {
+  if (RPL == 1) return (line & 7) ^ ((line >> 3) & 1);
+  return ((line >> 1) & 3) ^ ((line & 1) << 1);
 }
 
 struct GemmParams {
@@ -120,14 +140,17 @@ struct GemmParams {
 // bf16 grouped GEMM on the matrix cores.
 //
 // C[m][n] = sum_k A[m][k] * B[n][k]  (both operands contiguous along k).
-// Tile 128 rows x 256 weight rows, k-slices of 64 staged in LDS (double
-// buffered, 96 KiB), 4 waves in a 2x2 layout, each wave 64 rows x 128 weight
-// rows = 2 x 4 v_mfma_f32_32x32x16_bf16 accumulators.  In the gate/up pass the
-// 256 weight rows are 128 gate rows and the matching 128 up rows, so one lane
-// holds the gate and up value of the same output element and the SwiGLU (and
-// clip) is applied in registers before h is written once, in fp16.
-// LDS rows are 128 bytes; the 16-byte chunk c of row r sits at chunk c^(r&7) so
-// that the 32 rows read by one MFMA operand fetch spread over all banks.
+// A block computes BM rows x 256 weight rows; k-slices of BK are staged in LDS
+// (double buffered), 4 waves in a 2x2 layout, each wave (BM/2) rows x 128
+// weight rows = (BM/64) x 4 v_mfma_f32_32x32x16 accumulators.  In the gate/up
+// pass the 256 weight rows are 128 gate rows and the matching 128 up rows, so
+// one lane holds the gate and up value of the same output element and the
+// SwiGLU (and clip) is applied in registers before h is written once.
+//
+// LDS layout: 128-byte lines holding 128/(2*BK) rows (one row for BK = 64, two
+// for BK = 32); the 16-byte chunk at position q of line l is stored at position
+// q ^ lds_swizzle(l), so the rows one MFMA operand fetch reads spread over all
+// banks, and each thread's chunk of a staged row keeps one swizzled position.
 //
 // Number formats.  The gate/up pass multiplies bf16 x and bf16 weights; its
 // result h is stored in fp16, whose 11-bit significand rounds 8x finer than
@@ -137,13 +160,27 @@ struct GemmParams {
 // fp16's normal range, and within 2^-24 absolute below it.  Expert output rows
 // are written in fp16 as well.  With bf16 h and rows the rounding alone would
 // use most of the 2e-2 * RMS(y) error budget; with fp16 it uses about a tenth.
-constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int STAGE = (BM + BN) * BK;   // elements per LDS stage
+constexpr int BN = kGemmBN;
 
-template <int MODE>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sm[2 * STAGE];
+template <int MODE, int BM, int BK, int WM_, int WN_, int MINB>
+__global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams p) {
+  constexpr int NT = 64 * WM_ * WN_;          // threads
+  constexpr int KCH = BK / 8;                // 16-byte chunks per staged row
+  constexpr int RPL = 8 / KCH;               // rows per 128-byte LDS line
+  constexpr int STAGE = (BM + BN) * BK;      // elements per LDS stage
+  constexpr int RSTEP = NT / KCH;            // rows covered by one pass of the loaders
+  constexpr int NA = BM / RSTEP;             // A chunks per thread per stage
+  constexpr int NB = BN / RSTEP;             // B chunks per thread per stage
+  constexpr int WROWS = BM / WM_;            // rows per wave
+  constexpr int FM = WROWS / 32;             // A fragments (32 rows) per wave
+  constexpr int FN = BN / WN_ / 32;          // B fragments (32 weight rows) per wave
   constexpr int CT = (MODE == MODE_GATEUP) ? BN / 2 : BN;   // output columns per tile
+  constexpr int WCOLS = CT / WN_;            // output columns per wave
+  static_assert(NA * RSTEP == BM && NB * RSTEP == BN, "loader shape");
+  static_assert((RSTEP / RPL) % 8 == 0, "swizzle period");
+  static_assert(MODE != MODE_GATEUP || FN % 2 == 0, "gate/up fragments come in pairs");
+  __shared__ __attribute__((aligned(16))) uint16_t sm[2 * STAGE];
+
   const int ntn = (p.Ncols + CT - 1) / CT;
   const Tile tl = decode_tile(p.plan, p.G, ntn, BM, CT);
   if (!tl.ok) return;
@@ -158,14 +195,15 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmParams p) {
     B1 = static_cast<const uint16_t*>(routed ? p.Br1 : p.Bs1) +
          (int64_t)(routed ? tl.g : tl.g - p.n_gather) * p.wstride;
 
-  // ---- global -> register loaders: thread owns k-chunk kc of rows r0 + 32 i
-  const int kc = tid & 7;
-  const int r0 = tid >> 3;
-  const int swz = ((kc ^ (r0 & 7)) << 3);
-  const uint16_t* ag[4];
+  // ---- global -> register loaders: thread owns chunk kc of rows r0 + RSTEP*i
+  const int kc = tid % KCH;
+  const int r0 = tid / KCH;
+  // the swizzled position of (row, chunk) depends only on r0 for a thread's rows
+  const int sw_off = (((r0 % RPL) * KCH + kc) ^ lds_swizzle<RPL>(r0 / RPL)) << 3;
+  const uint16_t* ag[NA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int m = tl.m0 + r0 + 32 * i;
+  for (int i = 0; i < NA; ++i) {
+    int m = tl.m0 + r0 + RSTEP * i;
     if (m >= tl.M) m = tl.M - 1;
     int64_t arow;
     if (MODE == MODE_DOWN) {
@@ -178,10 +216,10 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmParams p) {
     }
     ag[i] = A + arow * p.ldA + kc * 8;
   }
-  const uint16_t* bg[8];
+  const uint16_t* bg[NB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int n = r0 + 32 * i;
+  for (int i = 0; i < NB; ++i) {
+    const int n = r0 + RSTEP * i;
     if (MODE == MODE_GATEUP) {
       int col = tl.n0 + (n & (CT - 1));
       if (col >= p.Ncols) col = p.Ncols - 1;
@@ -193,76 +231,91 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmParams p) {
     }
   }
 
-  u32x4_t ra[4], rbv[8];
-  auto gload = [&](int k0) {
+  // two register sets: a slice is loaded two compute phases before it is
+  // staged into LDS, so a global load has two slices of MFMA work to land
+  u32x4_t ra[2][NA], rbv[2][NB];
+  // full k-slices: unconditional loads (no branch, so the compiler's waits only
+  // cover the slice actually consumed); a ragged last slice zero-fills
+  auto load_full = [&](int kt, int set) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ra[set][i] = *reinterpret_cast<const u32x4_t*>(ag[i] + k0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) rbv[set][i] = *reinterpret_cast<const u32x4_t*>(bg[i] + k0);
+  };
+  auto load_tail = [&](int kt, int set) {
+    const int k0 = kt * BK;
     const bool ok = (k0 + kc * 8) < p.K;
     const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = ok ? *reinterpret_cast<const u32x4_t*>(ag[i] + k0) : z;
+    for (int i = 0; i < NA; ++i)
+      ra[set][i] = ok ? *reinterpret_cast<const u32x4_t*>(ag[i] + k0) : z;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rbv[i] = ok ? *reinterpret_cast<const u32x4_t*>(bg[i] + k0) : z;
+    for (int i = 0; i < NB; ++i)
+      rbv[set][i] = ok ? *reinterpret_cast<const u32x4_t*>(bg[i] + k0) : z;
   };
-  auto sstore = [&](int buf) {
-    uint16_t* s = sm + buf * STAGE;
+  // row r of the stage starts at line r / RPL
+  auto sstore = [&](uint16_t* s, int set) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4_t*>(s + (r0 + 32 * i) * BK + swz) = ra[i];
+    for (int i = 0; i < NA; ++i)
+      *reinterpret_cast<u32x4_t*>(s + ((r0 + RSTEP * i) / RPL) * 64 + sw_off) = ra[set][i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4_t v = rbv[i];
+    for (int i = 0; i < NB; ++i) {
+      u32x4_t v = rbv[set][i];
       if (MODE == MODE_DOWN) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = bf16x2_to_f16x2(v[q]);
       }
-      *reinterpret_cast<u32x4_t*>(s + BM * BK + (r0 + 32 * i) * BK + swz) = v;
+      *reinterpret_cast<u32x4_t*>(s + BM * BK + ((r0 + RSTEP * i) / RPL) * 64 + sw_off) = v;
     }
   };
 
-  // ---- MFMA fragment addressing
+  // ---- MFMA fragment addressing: lane supplies row (lane & 31) of a 32-row
+  // fragment and k-chunk kk*2 + (lane >> 5) of the slice
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM_, wn = wave / WM_;
   const int lr = lane & 31, lh = lane >> 5;
-  const int l7 = lane & 7;
-  int a_off[2], b_off[4];
+  const int lrow_part = lr % RPL;               // fragment bases are multiples of 32
+  const int lline = lr / RPL;
+  const int lswz = lds_swizzle<RPL>(lline);      // same for every fragment of this lane
+  int a_off[FM], b_off[FN], ksw[BK / 16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) a_off[i] = (wm * 64 + 32 * i + lr) * BK;
+  for (int i = 0; i < FM; ++i) a_off[i] = ((wm * WROWS + 32 * i) / RPL + lline) * 64;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int row;
-    if (MODE == MODE_GATEUP) row = (j >> 1) * CT + wn * 64 + 32 * (j & 1) + lr;
-    else row = wn * 128 + 32 * j + lr;
-    b_off[j] = BM * BK + row * BK;
+  for (int j = 0; j < FN; ++j) {
+    int base;
+    if (MODE == MODE_GATEUP)   // first half gate rows, second half the matching up rows
+      base = (j / (FN / 2)) * CT + wn * WCOLS + 32 * (j % (FN / 2));
+    else
+      base = wn * WCOLS + 32 * j;
+    b_off[j] = BM * BK + (base / RPL + lline) * 64;
   }
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) ksw[kk] = ((lrow_part * KCH + kk * 2 + lh) ^ lswz) << 3;
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = (p.K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const uint16_t* s = sm + cur * STAGE;
+  auto compute = [&](const uint16_t* s) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int sw = ((kk * 2 + lh) ^ l7) << 3;
-      u32x4_t af[2], bf[4];
+      u32x4_t af[FM], bf[FN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(s + a_off[i] + sw);
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const u32x4_t*>(s + a_off[i] + ksw[kk]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4_t*>(s + b_off[j] + sw);
+      for (int j = 0; j < FN; ++j)
+        bf[j] = *reinterpret_cast<const u32x4_t*>(s + b_off[j] + ksw[kk]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FN; ++j) {
           if (MODE == MODE_DOWN)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                 __builtin_bit_cast(f16x8_t, af[i]), __builtin_bit_cast(f16x8_t, bf[j]), acc[i][j],
@@ -273,28 +326,70 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmParams p) {
                 acc[i][j], 0, 0, 0);
         }
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+  };
+
+  // Main loop over the full k-slices, unrolled over the two LDS stages and
+  // register sets so their offsets are constants.  Iteration kt: load slice
+  // kt+2 into register set kt%2 (staged in the previous iteration), compute
+  // slice kt from stage kt%2, stage slice kt+1 (set (kt+1)%2) into stage
+  // (kt+1)%2.  A ragged last slice is staged and computed after the loop.
+  const int nfull = p.K / BK;
+  const bool ragged = (p.K % BK) != 0;
+  uint16_t* const s0 = sm;
+  uint16_t* const s1 = sm + STAGE;
+  if (nfull > 0) {
+    // Loads and stores below are unconditional (a slice index past the end is
+    // clamped to the last full slice and its copy is never read): straight-line
+    // code lets the compiler wait only for the loads of the slice being staged
+    // instead of for every load in flight.
+    const int last = nfull - 1;
+    load_full(0, 0);
+    load_full(min(1, last), 1);
+    sstore(s0, 0);
     __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= nfull; kt += 2) {
+      load_full(min(kt + 2, last), 0);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+      compute(s0);
+      sstore(s1, 1);
+      __syncthreads();
+      load_full(min(kt + 3, last), 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s1);
+      sstore(s0, 0);
+      __syncthreads();
+    }
+    if (kt < nfull) {          // odd count: the last full slice sits in stage 0
+      compute(s0);
+      __syncthreads();
+    }
+  }
+  if (ragged) {
+    load_tail(nfull, 0);
+    sstore(s0, 0);
+    __syncthreads();
+    compute(s0);
   }
 
   // ---- epilogue.  32x32 accumulator layout: element v of a lane is row
   // 8*(v/4) + 4*(lane/32) + v%4, column lane%32.
   uint16_t* C = static_cast<uint16_t*>(p.C);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int lrow = wm * 64 + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
+      const int lrow = wm * WROWS + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
       const int m = tl.m0 + lrow;
       if (m >= tl.M) continue;
       uint16_t* crow = C + (tl.rb + m) * p.ldC;
       if (MODE == MODE_GATEUP) {
 #pragma unroll
-        for (int jn = 0; jn < 2; ++jn) {
-          const int col = tl.n0 + wn * 64 + 32 * jn + lr;
+        for (int jn = 0; jn < FN / 2; ++jn) {
+          const int col = tl.n0 + wn * WCOLS + 32 * jn + lr;
           if (col < p.Ncols) {
             const float a = acc[i][jn][v];
-            const float u = acc[i][jn + 2][v];
+            const float u = acc[i][jn + FN / 2][v];
             float hv = a / (1.0f + __expf(-a)) * u;
             if (p.clip > 0.f) hv = fminf(fmaxf(hv, -p.clip), p.clip);
             crow[col] = f32_to_f16_sat(hv);
@@ -302,8 +397,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmParams p) {
         }
       } else {
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) {
-          const int col = tl.n0 + wn * 128 + 32 * jn + lr;
+        for (int jn = 0; jn < FN; ++jn) {
+          const int col = tl.n0 + wn * WCOLS + 32 * jn + lr;
           if (col < p.Ncols) {
             float vv = acc[i][jn][v];
             if (MODE == MODE_RELU_UP) vv = fmaxf(vv, 0.f);
@@ -426,8 +521,35 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(GemmParams p) {
   }
 }
 
+struct GemmCfg {
+  int bm, bk, wm, wn, minb;
+};
+
+// Tile configuration of the bf16 grouped GEMMs for one call.  Groups that
+// average at least 512 rows (many tokens per expert) use 256-row tiles with 8
+// waves (2 per SIMD, 64 KiB LDS); smaller groups use 128-row tiles with 4 waves
+// and two blocks per CU (48 KiB LDS each), which wastes less on ragged tails.
+GemmCfg choose_cfg(const FfnCall& c) {
+#ifdef MOE_CFG
+  (void)c;
+  return GemmCfg{MOE_CFG};
+#else
+  const int64_t groups = c.n_gather + c.n_ident;
+  const int64_t rows = c.routed_rows + c.n_ident * c.N;
+  const int64_t avg = groups > 0 ? rows / groups : 0;
+  if (avg >= 512) return GemmCfg{256, 32, 2, 4, 1};
+  return GemmCfg{128, 32, 2, 2, 2};
+#endif
+}
+
+template <int MODE, int BMv, int BKv, int WMv, int WNv, int MINBv>
+void launch_bf16(const GemmParams& gp, int64_t blocks, hipStream_t s) {
+  ffn_gemm_bf16<MODE, BMv, BKv, WMv, WNv, MINBv><<<(unsigned)blocks, 64 * WMv * WNv, 0, s>>>(gp);
+}
+
 template <int MODE>
-hipError_t launch_gemm(const GemmParams& gp, int dtype, int64_t max_mtiles, hipStream_t s) {
+hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int64_t max_mtiles,
+                       hipStream_t s) {
   int CT;
   if (dtype == MOE_BF16) CT = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   else CT = kF32BN;
@@ -435,25 +557,40 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, int64_t max_mtiles, hipS
   int64_t blocks = max_mtiles * ntn;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks <= 0) return hipSuccess;
-  if (dtype == MOE_BF16) ffn_gemm_bf16<MODE><<<(unsigned)blocks, 256, 0, s>>>(gp);
-  else ffn_gemm_f32<MODE><<<(unsigned)blocks, 256, 0, s>>>(gp);
+  if (dtype == MOE_BF16) {
+#define MOE_TRY(a, b, c, d, e)                                                          \
+  if (cfg.bm == a && cfg.bk == b && cfg.wm == c && cfg.wn == d && cfg.minb == e)        \
+    launch_bf16<MODE, a, b, c, d, e>(gp, blocks, s);                                    \
+  else
+    MOE_TRY(128, 32, 2, 2, 2)
+    MOE_TRY(128, 64, 2, 2, 1)
+    MOE_TRY(256, 32, 2, 4, 1)
+    MOE_TRY(128, 64, 2, 4, 1)
+    return hipErrorInvalidValue;
+#undef MOE_TRY
+  } else {
+    ffn_gemm_f32<MODE><<<(unsigned)blocks, 256, 0, s>>>(gp);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int64_t ffn_max_mtiles(int64_t N, int k, int E, int S, int dtype) {
-  const int bm = dtype == MOE_BF16 ? kGemmBM : kF32BM;
+// Upper bound on the m-tiles of a call: each routed group adds at most one
+// partial tile beyond routed_rows / bm.
+static int64_t max_mtiles(const FfnCall& c, int bm) {
   int64_t t = 0;
-  if (E > 0) t += (N * k + bm - 1) / bm + E;
-  t += (int64_t)S * ((N + bm - 1) / bm);
+  if (c.n_gather > 0) t += (c.routed_rows + bm - 1) / bm + c.n_gather;
+  t += (int64_t)c.n_ident * ((c.N + bm - 1) / bm);
   return t;
 }
 
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   const int G = c.n_gather + c.n_ident;
   if (G <= 0 || c.N <= 0) return hipSuccess;
-  const int bm = c.dtype == MOE_BF16 ? kGemmBM : kF32BM;
+  const GemmCfg cfg = c.dtype == MOE_BF16 ? choose_cfg(c) : GemmCfg{kF32BM, 16, 1, 1, 1};
+  const int bm = cfg.bm;
+  const int64_t mt = max_mtiles(c, bm);
   const int64_t rows_cap = c.routed_rows;
   auto mark = [&](int i) {
     if (c.marks[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(c.marks[i]), s);
@@ -482,10 +619,10 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   mark(2);
   if (c.activation == MOE_SWIGLU) {
     up.Br0 = c.wg; up.Br1 = c.wu; up.Bs0 = c.sg; up.Bs1 = c.su;
-    err = launch_gemm<MODE_GATEUP>(up, c.dtype, c.max_tiles_m, s);
+    err = launch_gemm<MODE_GATEUP>(up, c.dtype, cfg, mt, s);
   } else {
     up.Br0 = c.wu; up.Bs0 = c.su;
-    err = launch_gemm<MODE_RELU_UP>(up, c.dtype, c.max_tiles_m, s);
+    err = launch_gemm<MODE_RELU_UP>(up, c.dtype, cfg, mt, s);
   }
   if (err != hipSuccess) return err;
   mark(3);
@@ -505,7 +642,7 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   dn.Bs0 = c.sd;
   dn.C = c.y_rows;
   mark(4);
-  err = launch_gemm<MODE_DOWN>(dn, c.dtype, c.max_tiles_m, s);
+  err = launch_gemm<MODE_DOWN>(dn, c.dtype, cfg, mt, s);
   mark(5);
   return err;
 }

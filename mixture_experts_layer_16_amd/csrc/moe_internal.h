@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -97,11 +97,9 @@ struct FfnCall {
   void* h;                     // [rows][I]
   void* y_rows;                // [rows][d]
   int32_t* plan;               // workspace for the tile plan
-  int64_t max_tiles_m;         // host upper bound on m-tiles (grid sizing)
   void* marks[6];              // optional hipEvent_t: before/after plan, gate/up, down
 };
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
-int64_t ffn_max_mtiles(int64_t N, int k, int E, int S, int dtype);
 
 hipError_t launch_combine(int dtype, const void* y_rows, const int32_t* row_of,
                           const float* topk_w, const void* y_shared, int64_t shared_stride_rows,

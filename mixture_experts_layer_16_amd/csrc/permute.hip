@@ -14,9 +14,10 @@
 //               expert), keeps per-wave running counts in LDS, then turns them
 //               into block-local ranks and a per-block histogram (also split by
 //               modality);
-//   2. scan:    per expert, an exclusive scan of the block histograms gives each
-//               block's base rank and the expert's demand; kept = min(demand, C);
-//               an exclusive scan over experts gives the offsets;
+//   2. scan:    per expert (one wave each), an exclusive scan of the block
+//               histograms gives each block's base rank and the expert's demand;
+//               kept = min(demand, C); an exclusive scan over experts gives the
+//               offsets;
 //   3. scatter: rank = block base + local rank; kept iff rank < C.
 #include "moe_internal.h"
 
@@ -94,27 +95,51 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(
   }
 }
 
+// One wave per expert: the block histograms are scanned 64 blocks at a time
+// with a wave prefix sum and a running carry.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(
     int32_t* __restrict__ blk, int nblk, int32_t* __restrict__ counts,
     int32_t* __restrict__ mod_counts, int32_t* __restrict__ offsets, int E, int64_t C) {
   __shared__ int32_t kept[kMaxExperts];
   __shared__ int32_t tmp[1024];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0, m0 = 0, m1 = 0;
-    for (int b = 0; b < nblk; ++b) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  for (int e = wave; e < E; e += nwaves) {
+    int carry = 0, m0 = 0, m1 = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 64) {
+      const int b = b0 + lane;
       int32_t* rec = blk + (int64_t)b * 3 * E;
-      const int v = rec[e];
-      rec[e] = run;
-      run += v;
-      m0 += rec[E + e];
-      m1 += rec[2 * E + e];
+      int v = 0, a0 = 0, a1 = 0;
+      if (b < nblk) {
+        v = rec[e];
+        a0 = rec[E + e];
+        a1 = rec[2 * E + e];
+      }
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      if (b < nblk) rec[e] = carry + incl - v;
+      carry += __shfl(incl, 63);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        a0 += __shfl_xor(a0, off);
+        a1 += __shfl_xor(a1, off);
+      }
+      m0 += a0;
+      m1 += a1;
     }
-    counts[e] = run;
-    if (mod_counts) {
-      mod_counts[e] = m0;
-      mod_counts[E + e] = m1;
+    if (lane == 0) {
+      counts[e] = carry;
+      if (mod_counts) {
+        mod_counts[e] = m0;
+        mod_counts[E + e] = m1;
+      }
+      kept[e] = (C < 0 || carry < C) ? carry : (int)C;
     }
-    kept[e] = (C < 0 || run < C) ? run : (int)C;
   }
   __syncthreads();
   const int total = block_exclusive_scan_1024(kept, E, tmp);

@@ -114,12 +114,13 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 // top-k: one token per wavefront.  Lane l owns experts l, l+64, l+128, ...
 // Each of the k rounds is a 64-lane argmax on (key desc, index asc) by xor
 // butterflies; lane r keeps the r-th winner.  Keys and scores are float64.
-constexpr int TK_MAXJ = kMaxExperts / 64;
-
 __device__ __forceinline__ bool better(double ka, int ea, double kb, int eb) {
   return ka > kb || (ka == kb && ea < eb);
 }
 
+// J = key slots per lane (E <= 64 * J), a compile-time constant so the keys
+// stay in registers.
+template <int J>
 __global__ __launch_bounds__(256) void topk_kernel(
     const double* __restrict__ z, const float* __restrict__ sel_bias,
     const uint8_t* __restrict__ modality, int n_bias_sets, int gating,
@@ -132,10 +133,10 @@ __global__ __launch_bounds__(256) void topk_kernel(
   const float* bias = n_bias_sets ? sel_bias + (int64_t)m * E : nullptr;
   const bool sig = (gating == MOE_SIGMOID);
 
-  double key[TK_MAXJ], sc[TK_MAXJ];
+  double key[J], sc[J];
   uint32_t valid = 0;
 #pragma unroll
-  for (int j = 0; j < TK_MAXJ; ++j) {
+  for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
     key[j] = -INFINITY;
     sc[j] = 0.0;
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
     double bk = -INFINITY, bs = 0.0;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < TK_MAXJ; ++j) {
+    for (int j = 0; j < J; ++j) {
       if (valid & (1u << j)) {
         const int e = lane + 64 * j;
         if (better(key[j], e, bk, be)) { bk = key[j]; be = e; bs = sc[j]; }
@@ -215,8 +216,18 @@ hipError_t launch_router_f32(const float* x, const float* w, const float* logit_
 hipError_t launch_topk(const double* z, const float* sel_bias, const uint8_t* modality,
                        int n_bias_sets, int gating, int32_t* idx, float* w, int64_t N,
                        int E, int k, hipStream_t s) {
-  topk_kernel<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(z, sel_bias, modality, n_bias_sets,
-                                                       gating, idx, w, N, E, k);
+  const unsigned grid = (unsigned)((N + 3) / 4);
+  const int J = (E + 63) / 64;
+#define MOE_TOPK(JJ)                                                                        \
+  topk_kernel<JJ><<<grid, 256, 0, s>>>(z, sel_bias, modality, n_bias_sets, gating, idx, w, N, \
+                                       E, k)
+  if (J <= 1) MOE_TOPK(1);
+  else if (J <= 2) MOE_TOPK(2);
+  else if (J <= 4) MOE_TOPK(4);
+  else if (J <= 6) MOE_TOPK(6);
+  else if (J <= 8) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 

@@ -162,7 +162,7 @@ struct GemmParams {
 // use most of the 2e-2 * RMS(y) error budget; with fp16 it uses about a tenth.
 constexpr int BN = kGemmBN;
 
-template <int MODE, int BM, int BK, int WM_, int WN_, int MINB>
+template <int MODE, int BM, int BK, int WM_, int WN_, int MINB, int NSETS, int FRAGDB>
 __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams p) {
   constexpr int NT = 64 * WM_ * WN_;          // threads
   constexpr int KCH = BK / 8;                // 16-byte chunks per staged row
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
 
   // two register sets: a slice is loaded two compute phases before it is
   // staged into LDS, so a global load has two slices of MFMA work to land
-  u32x4_t ra[2][NA], rbv[2][NB];
+  u32x4_t ra[NSETS][NA], rbv[NSETS][NB];
   // full k-slices: unconditional loads (no branch, so the compiler's waits only
   // cover the slice actually consumed); a ragged last slice zero-fills
   auto load_full = [&](int kt, int set) {
@@ -302,29 +302,44 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  auto mfmas = [&](const u32x4_t (&af)[FM], const u32x4_t (&bf)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if (MODE == MODE_DOWN)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8_t, af[i]), __builtin_bit_cast(f16x8_t, bf[j]), acc[i][j],
+              0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, bf[j]),
+              acc[i][j], 0, 0, 0);
+      }
+  };
+  auto read_frags = [&](const uint16_t* s, int kk, u32x4_t (&af)[FM], u32x4_t (&bf)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(s + a_off[i] + ksw[kk]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const u32x4_t*>(s + b_off[j] + ksw[kk]);
+  };
   auto compute = [&](const uint16_t* s) {
+    if (FRAGDB) {
+      // fragments of step kk+1 are read while the MFMAs of step kk run
+      u32x4_t af[2][FM], bf[2][FN];
+      read_frags(s, 0, af[0], bf[0]);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      u32x4_t af[FM], bf[FN];
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        if (kk + 1 < BK / 16) read_frags(s, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+        mfmas(af[kk & 1], bf[kk & 1]);
+      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const u32x4_t*>(s + a_off[i] + ksw[kk]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bf[j] = *reinterpret_cast<const u32x4_t*>(s + b_off[j] + ksw[kk]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if (MODE == MODE_DOWN)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8_t, af[i]), __builtin_bit_cast(f16x8_t, bf[j]), acc[i][j],
-                0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, bf[j]),
-                acc[i][j], 0, 0, 0);
-        }
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        u32x4_t af[FM], bf[FN];
+        read_frags(s, kk, af, bf);
+        mfmas(af, bf);
+      }
     }
   };
 
@@ -343,26 +358,50 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
     // code lets the compiler wait only for the loads of the slice being staged
     // instead of for every load in flight.
     const int last = nfull - 1;
-    load_full(0, 0);
-    load_full(min(1, last), 1);
-    sstore(s0, 0);
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 2 <= nfull; kt += 2) {
-      load_full(min(kt + 2, last), 0);
-      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
-      compute(s0);
-      sstore(s1, 1);
-      __syncthreads();
-      load_full(min(kt + 3, last), 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(s1);
+    if (NSETS == 2) {
+      load_full(0, 0);
+      load_full(min(1, last), NSETS - 1);
       sstore(s0, 0);
       __syncthreads();
-    }
-    if (kt < nfull) {          // odd count: the last full slice sits in stage 0
-      compute(s0);
+      int kt = 0;
+      for (; kt + 2 <= nfull; kt += 2) {
+        load_full(min(kt + 2, last), 0);
+        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+        compute(s0);
+        sstore(s1, NSETS - 1);
+        __syncthreads();
+        load_full(min(kt + 3, last), NSETS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s1);
+        sstore(s0, 0);
+        __syncthreads();
+      }
+      if (kt < nfull) {          // odd count: the last full slice sits in stage 0
+        compute(s0);
+        __syncthreads();
+      }
+    } else {
+      // one register set: slice kt+1 is loaded while slice kt is computed
+      load_full(0, 0);
+      sstore(s0, 0);
       __syncthreads();
+      int kt = 0;
+      for (; kt + 2 <= nfull; kt += 2) {
+        load_full(kt + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s0);
+        sstore(s1, 0);
+        __syncthreads();
+        load_full(min(kt + 2, last), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s1);
+        sstore(s0, 0);
+        __syncthreads();
+      }
+      if (kt < nfull) {
+        compute(s0);
+        __syncthreads();
+      }
     }
   }
   if (ragged) {
@@ -522,7 +561,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(GemmParams p) {
 }
 
 struct GemmCfg {
-  int bm, bk, wm, wn, minb;
+  int bm, bk, wm, wn, minb, nsets, fragdb;
 };
 
 // Tile configuration of the bf16 grouped GEMMs for one call.  Groups that
@@ -537,14 +576,15 @@ GemmCfg choose_cfg(const FfnCall& c) {
   const int64_t groups = c.n_gather + c.n_ident;
   const int64_t rows = c.routed_rows + c.n_ident * c.N;
   const int64_t avg = groups > 0 ? rows / groups : 0;
-  if (avg >= 512) return GemmCfg{256, 32, 2, 4, 1};
-  return GemmCfg{128, 32, 2, 2, 2};
+  if (avg >= 512) return GemmCfg{256, 32, 2, 4, 1, 2, 0};
+  return GemmCfg{128, 32, 2, 2, 2, 2, 0};
 #endif
 }
 
-template <int MODE, int BMv, int BKv, int WMv, int WNv, int MINBv>
+template <int MODE, int BMv, int BKv, int WMv, int WNv, int MINBv, int NS, int FD>
 void launch_bf16(const GemmParams& gp, int64_t blocks, hipStream_t s) {
-  ffn_gemm_bf16<MODE, BMv, BKv, WMv, WNv, MINBv><<<(unsigned)blocks, 64 * WMv * WNv, 0, s>>>(gp);
+  ffn_gemm_bf16<MODE, BMv, BKv, WMv, WNv, MINBv, NS, FD>
+      <<<(unsigned)blocks, 64 * WMv * WNv, 0, s>>>(gp);
 }
 
 template <int MODE>
@@ -558,14 +598,18 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks <= 0) return hipSuccess;
   if (dtype == MOE_BF16) {
-#define MOE_TRY(a, b, c, d, e)                                                          \
-  if (cfg.bm == a && cfg.bk == b && cfg.wm == c && cfg.wn == d && cfg.minb == e)        \
-    launch_bf16<MODE, a, b, c, d, e>(gp, blocks, s);                                    \
+#define MOE_TRY(a, b, c, d, e, f, g)                                                    \
+  if (cfg.bm == a && cfg.bk == b && cfg.wm == c && cfg.wn == d && cfg.minb == e &&      \
+      cfg.nsets == f && cfg.fragdb == g)                                                \
+    launch_bf16<MODE, a, b, c, d, e, f, g>(gp, blocks, s);                              \
   else
-    MOE_TRY(128, 32, 2, 2, 2)
-    MOE_TRY(128, 64, 2, 2, 1)
-    MOE_TRY(256, 32, 2, 4, 1)
-    MOE_TRY(128, 64, 2, 4, 1)
+    MOE_TRY(128, 32, 2, 2, 2, 2, 0)
+    MOE_TRY(256, 32, 2, 4, 1, 2, 0)
+#ifdef MOE_CFG
+#define MOE_TRY_CFG(...) MOE_TRY(__VA_ARGS__)
+    MOE_TRY_CFG(MOE_CFG)
+#undef MOE_TRY_CFG
+#endif
     return hipErrorInvalidValue;
 #undef MOE_TRY
   } else {
@@ -588,7 +632,7 @@ static int64_t max_mtiles(const FfnCall& c, int bm) {
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   const int G = c.n_gather + c.n_ident;
   if (G <= 0 || c.N <= 0) return hipSuccess;
-  const GemmCfg cfg = c.dtype == MOE_BF16 ? choose_cfg(c) : GemmCfg{kF32BM, 16, 1, 1, 1};
+  const GemmCfg cfg = c.dtype == MOE_BF16 ? choose_cfg(c) : GemmCfg{kF32BM, 16, 1, 1, 1, 1, 0};
   const int bm = cfg.bm;
   const int64_t mt = max_mtiles(c, bm);
   const int64_t rows_cap = c.routed_rows;

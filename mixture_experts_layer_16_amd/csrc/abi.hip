@@ -22,7 +22,11 @@ WsLayout ws_layout(const moe_problem* p) {
     off += align256(bytes ? bytes : 1);
     return o;
   };
-  L.logits = take(N * E * 8);
+  const size_t nsplit =
+      p->dtype == MOE_BF16
+          ? (size_t)router_splits_used(p->d_model, router_splits((int64_t)N, p->d_model, (int)E))
+          : 1;
+  L.logits = take(nsplit * N * E * 8);
   L.topk_idx = take(nk * 4);
   L.topk_w = take(nk * 4);
   L.counts = take(E * 4);
@@ -93,21 +97,37 @@ static int64_t capacity_of(const moe_problem* p) {
 
 static inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Router + top-k.  zpart: workspace for the float64 partial logits
+// (route_partials_bytes); z_out (nullable): receives the logits.
+static int route_splits(const moe_problem* p) {
+  return p->dtype == MOE_BF16
+             ? router_splits_used(p->d_model,
+                                  router_splits(p->n_tokens, p->d_model, p->n_experts))
+             : 1;
+}
+static size_t route_partials_bytes(const moe_problem* p) {
+  return (size_t)route_splits(p) * (size_t)p->n_tokens * p->n_experts * 8;
+}
+
 static int run_route(const moe_problem* p, const void* x, const void* w_router,
                      const float* logit_bias, const float* sel_bias, const uint8_t* modality,
-                     int32_t* idx, float* w, double* z, hipStream_t s) {
+                     int32_t* idx, float* w, double* zpart, double* z_out, hipStream_t s) {
   const int64_t N = p->n_tokens;
   hipError_t err;
-  if (p->dtype == MOE_BF16)
+  int used = 1;
+  if (p->dtype == MOE_BF16) {
+    const int ns = router_splits(N, p->d_model, p->n_experts);
+    used = router_splits_used(p->d_model, ns);
     err = launch_router_bf16(static_cast<const uint16_t*>(x),
-                             static_cast<const uint16_t*>(w_router), logit_bias, z, N,
-                             p->d_model, p->n_experts, s);
-  else
+                             static_cast<const uint16_t*>(w_router), zpart, ns, N, p->d_model,
+                             p->n_experts, s);
+  } else {
     err = launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
-                            logit_bias, z, N, p->d_model, p->n_experts, s);
+                            zpart, N, p->d_model, p->n_experts, s);
+  }
   if (err != hipSuccess) return MOE_ERR_HIP;
-  err = launch_topk(z, p->n_bias_sets ? sel_bias : nullptr, modality, p->n_bias_sets, p->gating,
-                    idx, w, N, p->n_experts, p->top_k, s);
+  err = launch_topk(zpart, used, logit_bias, z_out, p->n_bias_sets ? sel_bias : nullptr, modality,
+                    p->n_bias_sets, p->gating, idx, w, N, p->n_experts, p->top_k, s);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -163,11 +183,15 @@ int moe_route(const moe_problem* p, const void* x, const void* w_router, const f
   if (!topk_idx || !topk_w) return MOE_ERR_NULL;
   st = check_route_inputs(p, x, w_router, sel_bias, modality);
   if (st) return st;
-  const size_t need = logits ? 0 : (size_t)p->n_tokens * p->n_experts * 8;
+  // the partial logits go to the workspace, except when there is one partial
+  // and the caller's logits buffer can hold it (then the offset is added in place)
+  const bool in_place = logits && route_splits(p) == 1;
+  const size_t need = in_place ? 0 : route_partials_bytes(p);
   if (need && (!ws || ws_bytes < need)) return ws ? MOE_ERR_WORKSPACE : MOE_ERR_NULL;
   if (p->n_tokens == 0) return MOE_OK;
-  double* z = logits ? logits : static_cast<double*>(ws);
-  return run_route(p, x, w_router, logit_bias, sel_bias, modality, topk_idx, topk_w, z, S(stream));
+  double* zpart = in_place ? logits : static_cast<double*>(ws);
+  return run_route(p, x, w_router, logit_bias, sel_bias, modality, topk_idx, topk_w, zpart, logits,
+                   S(stream));
 }
 
 int moe_permute(const moe_problem* p, const int32_t* topk_idx, const uint8_t* modality,
@@ -310,7 +334,7 @@ int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
   char* base = static_cast<char*>(ws);
   const moe_routing none{};
   const moe_routing& r = routing_out ? *routing_out : none;
-  double* z = r.logits ? r.logits : reinterpret_cast<double*>(base + L.logits);
+  double* zpart = reinterpret_cast<double*>(base + L.logits);
   int32_t* idx = r.topk_idx ? r.topk_idx : reinterpret_cast<int32_t*>(base + L.topk_idx);
   float* gw = r.topk_w ? r.topk_w : reinterpret_cast<float*>(base + L.topk_w);
   int32_t* counts = r.counts ? r.counts : reinterpret_cast<int32_t*>(base + L.counts);
@@ -324,7 +348,7 @@ int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
     if (prof && prof->ev[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(prof->ev[i]), s);
   };
   mark(2 * MOE_STAGE_ROUTE);
-  st = run_route(p, x, w->w_router, logit_bias, sel_bias, modality, idx, gw, z, s);
+  st = run_route(p, x, w->w_router, logit_bias, sel_bias, modality, idx, gw, zpart, r.logits, s);
   if (st) return st;
   mark(2 * MOE_STAGE_ROUTE + 1);
   mark(2 * MOE_STAGE_PERMUTE);

@@ -140,12 +140,12 @@ struct GemmParams {
 // bf16 grouped GEMM on the matrix cores.
 //
 // C[m][n] = sum_k A[m][k] * B[n][k]  (both operands contiguous along k).
-// A block computes BM rows x 256 weight rows; k-slices of BK are staged in LDS
-// (double buffered), 4 waves in a 2x2 layout, each wave (BM/2) rows x 128
-// weight rows = (BM/64) x 4 v_mfma_f32_32x32x16 accumulators.  In the gate/up
-// pass the 256 weight rows are 128 gate rows and the matching 128 up rows, so
-// one lane holds the gate and up value of the same output element and the
-// SwiGLU (and clip) is applied in registers before h is written once.
+// A block computes BM rows x BN weight rows; k-slices of BK are staged in LDS
+// (double buffered); WM x WN waves, each (BM/WM) rows x (BN/WN) weight rows of
+// v_mfma_f32_32x32x16 accumulators.  In the gate/up pass the BN weight rows are
+// BN/2 gate rows and the matching BN/2 up rows, so one lane holds the gate and
+// up value of the same output element and the SwiGLU (and clip) is applied in
+// registers before h is written once.
 //
 // LDS layout: 128-byte lines holding 128/(2*BK) rows (one row for BK = 64, two
 // for BK = 32); the 16-byte chunk at position q of line l is stored at position
@@ -160,9 +160,7 @@ struct GemmParams {
 // fp16's normal range, and within 2^-24 absolute below it.  Expert output rows
 // are written in fp16 as well.  With bf16 h and rows the rounding alone would
 // use most of the 2e-2 * RMS(y) error budget; with fp16 it uses about a tenth.
-constexpr int BN = kGemmBN;
-
-template <int MODE, int BM, int BK, int WM_, int WN_, int MINB, int NSETS, int FRAGDB>
+template <int MODE, int BM, int BN, int BK, int WM_, int WN_, int MINB, int NSETS, int FRAGDB>
 __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams p) {
   constexpr int NT = 64 * WM_ * WN_;          // threads
   constexpr int KCH = BK / 8;                // 16-byte chunks per staged row
@@ -561,50 +559,68 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(GemmParams p) {
 }
 
 struct GemmCfg {
-  int bm, bk, wm, wn, minb, nsets, fragdb;
+  int bm, bn, bk, wm, wn, minb, nsets, fragdb;
 };
 
-// Tile configuration of the bf16 grouped GEMMs for one call.  Groups that
-// average at least 512 rows (many tokens per expert) use 256-row tiles with 8
-// waves (2 per SIMD, 64 KiB LDS); smaller groups use 128-row tiles with 4 waves
-// and two blocks per CU (48 KiB LDS each), which wastes less on ragged tails.
-GemmCfg choose_cfg(const FfnCall& c) {
+// Tile configuration of the bf16 grouped GEMMs for one call (both passes use
+// the same row tiling BM, since they share one tile plan).
+//  * decode-sized groups (at most 32 rows on average): 32-row tiles, so the
+//    matrix cores do not multiply padding rows; the weights stream through LDS
+//    with two slices in flight; the down pass uses 128-wide weight tiles so
+//    enough blocks run when d is small relative to the CU count;
+//  * groups averaging at least 512 rows: 256-row tiles, 8 waves (2 per SIMD);
+//  * otherwise 128-row tiles, 4 waves, two blocks per CU.
+GemmCfg choose_cfg(const FfnCall& c, int mode) {
 #ifdef MOE_CFG
   (void)c;
+  (void)mode;
   return GemmCfg{MOE_CFG};
 #else
   const int64_t groups = c.n_gather + c.n_ident;
   const int64_t rows = c.routed_rows + c.n_ident * c.N;
   const int64_t avg = groups > 0 ? rows / groups : 0;
-  if (avg >= 512) return GemmCfg{256, 32, 2, 4, 1, 2, 0};
-  return GemmCfg{128, 32, 2, 2, 2, 2, 0};
+  if (c.N <= 64) {
+    if (mode == MODE_DOWN) return GemmCfg{32, 128, 64, 1, 4, 2, 2, 0};
+    return GemmCfg{32, 256, 64, 1, 4, 2, 2, 0};
+  }
+  if (avg >= 512) return GemmCfg{256, 256, 32, 2, 4, 1, 2, 0};
+  return GemmCfg{128, 256, 32, 2, 2, 2, 2, 0};
 #endif
 }
 
-template <int MODE, int BMv, int BKv, int WMv, int WNv, int MINBv, int NS, int FD>
+// a configuration is usable by a pass if the gate/up fragments pair up
+template <int MODE, int BNv, int WNv>
+constexpr bool cfg_valid() {
+  return MODE != MODE_GATEUP || ((BNv / WNv / 32) % 2 == 0 && BNv / WNv / 32 >= 2);
+}
+
+template <int MODE, int BMv, int BNv, int BKv, int WMv, int WNv, int MINBv, int NS, int FD>
 void launch_bf16(const GemmParams& gp, int64_t blocks, hipStream_t s) {
-  ffn_gemm_bf16<MODE, BMv, BKv, WMv, WNv, MINBv, NS, FD>
-      <<<(unsigned)blocks, 64 * WMv * WNv, 0, s>>>(gp);
+  if constexpr (cfg_valid<MODE, BNv, WNv>())
+    ffn_gemm_bf16<MODE, BMv, BNv, BKv, WMv, WNv, MINBv, NS, FD>
+        <<<(unsigned)blocks, 64 * WMv * WNv, 0, s>>>(gp);
 }
 
 template <int MODE>
 hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int64_t max_mtiles,
                        hipStream_t s) {
   int CT;
-  if (dtype == MOE_BF16) CT = (MODE == MODE_GATEUP) ? BN / 2 : BN;
+  if (dtype == MOE_BF16) CT = (MODE == MODE_GATEUP) ? cfg.bn / 2 : cfg.bn;
   else CT = kF32BN;
   const int64_t ntn = (gp.Ncols + CT - 1) / CT;
   int64_t blocks = max_mtiles * ntn;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks <= 0) return hipSuccess;
   if (dtype == MOE_BF16) {
-#define MOE_TRY(a, b, c, d, e, f, g)                                                    \
-  if (cfg.bm == a && cfg.bk == b && cfg.wm == c && cfg.wn == d && cfg.minb == e &&      \
-      cfg.nsets == f && cfg.fragdb == g)                                                \
-    launch_bf16<MODE, a, b, c, d, e, f, g>(gp, blocks, s);                              \
+#define MOE_TRY(a, n, b, c, d, e, f, g)                                                 \
+  if (cfg.bm == a && cfg.bn == n && cfg.bk == b && cfg.wm == c && cfg.wn == d &&        \
+      cfg.minb == e && cfg.nsets == f && cfg.fragdb == g)                               \
+    launch_bf16<MODE, a, n, b, c, d, e, f, g>(gp, blocks, s);                           \
   else
-    MOE_TRY(128, 32, 2, 2, 2, 2, 0)
-    MOE_TRY(256, 32, 2, 4, 1, 2, 0)
+    MOE_TRY(128, 256, 32, 2, 2, 2, 2, 0)
+    MOE_TRY(256, 256, 32, 2, 4, 1, 2, 0)
+    MOE_TRY(32, 256, 64, 1, 4, 2, 2, 0)
+    MOE_TRY(32, 128, 64, 1, 4, 2, 2, 0)
 #ifdef MOE_CFG
 #define MOE_TRY_CFG(...) MOE_TRY(__VA_ARGS__)
     MOE_TRY_CFG(MOE_CFG)
@@ -632,8 +648,11 @@ static int64_t max_mtiles(const FfnCall& c, int bm) {
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   const int G = c.n_gather + c.n_ident;
   if (G <= 0 || c.N <= 0) return hipSuccess;
-  const GemmCfg cfg = c.dtype == MOE_BF16 ? choose_cfg(c) : GemmCfg{kF32BM, 16, 1, 1, 1, 1, 0};
-  const int bm = cfg.bm;
+  const GemmCfg cfg_up =
+      c.dtype == MOE_BF16 ? choose_cfg(c, MODE_GATEUP) : GemmCfg{kF32BM, kF32BN, 16, 1, 1, 1, 1, 0};
+  const GemmCfg cfg_dn =
+      c.dtype == MOE_BF16 ? choose_cfg(c, MODE_DOWN) : GemmCfg{kF32BM, kF32BN, 16, 1, 1, 1, 1, 0};
+  const int bm = cfg_up.bm;
   const int64_t mt = max_mtiles(c, bm);
   const int64_t rows_cap = c.routed_rows;
   auto mark = [&](int i) {
@@ -663,10 +682,10 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   mark(2);
   if (c.activation == MOE_SWIGLU) {
     up.Br0 = c.wg; up.Br1 = c.wu; up.Bs0 = c.sg; up.Bs1 = c.su;
-    err = launch_gemm<MODE_GATEUP>(up, c.dtype, cfg, mt, s);
+    err = launch_gemm<MODE_GATEUP>(up, c.dtype, cfg_up, mt, s);
   } else {
     up.Br0 = c.wu; up.Bs0 = c.su;
-    err = launch_gemm<MODE_RELU_UP>(up, c.dtype, cfg, mt, s);
+    err = launch_gemm<MODE_RELU_UP>(up, c.dtype, cfg_up, mt, s);
   }
   if (err != hipSuccess) return err;
   mark(3);
@@ -686,7 +705,7 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   dn.Bs0 = c.sd;
   dn.C = c.y_rows;
   mark(4);
-  err = launch_gemm<MODE_DOWN>(dn, c.dtype, cfg, mt, s);
+  err = launch_gemm<MODE_DOWN>(dn, c.dtype, cfg_dn, mt, s);
   mark(5);
   return err;
 }

@@ -13,22 +13,20 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // tiling constants shared by the host planner and the kernels
 
-constexpr int kGemmBM = 128;       // rows (tokens) per grouped-GEMM tile
-constexpr int kGemmBN = 256;       // weight rows per tile (gate+up: 128 + 128)
-constexpr int kGemmBK = 64;        // reduction slice staged in LDS
 constexpr int kF32BM = 64;         // fp32 path tile
 constexpr int kF32BN = 64;
 constexpr int kPermTokens = 256;   // tokens per block of the rank kernel
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
-constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kXcds = 8;
+constexpr int kMaxRouterSplits = 32;  // split-K pieces of the router for small batches           // MI355X: 8 accelerator complex dies, one L2 each
 
 // ---------------------------------------------------------------------------
 // device workspace layout (byte offsets from the workspace base)
 
 struct WsLayout {
-  size_t logits;        // f64 [N][E]
+  size_t logits;        // f64 [splits][N][E] router partial sums
   size_t topk_idx;      // i32 [N*k]
   size_t topk_w;        // f32 [N*k]
   size_t counts;        // i32 [E]
@@ -61,13 +59,20 @@ inline PlanView plan_view(int32_t* plan, int G) {
 // ---------------------------------------------------------------------------
 // launchers (each enqueues on `stream`, returns hipError_t of the launch)
 
-hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* w, const float* logit_bias,
-                              double* z, int64_t N, int d, int E, hipStream_t s);
-hipError_t launch_router_f32(const float* x, const float* w, const float* logit_bias,
-                             double* z, int64_t N, int d, int E, hipStream_t s);
-hipError_t launch_topk(const double* z, const float* sel_bias, const uint8_t* modality,
-                       int n_bias_sets, int gating, int32_t* idx, float* w, int64_t N,
-                       int E, int k, hipStream_t s);
+// Router logits as float64 partial sums over `nsplit` pieces of d
+// ([nsplit][N][E]); router_splits() picks nsplit for a problem and
+// router_splits_used() the number of pieces actually launched.
+int router_splits(int64_t N, int d, int E);
+int router_splits_used(int d, int nsplit);
+hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* w, double* zpart, int nsplit,
+                              int64_t N, int d, int E, hipStream_t s);
+hipError_t launch_router_f32(const float* x, const float* w, double* z, int64_t N, int d, int E,
+                             hipStream_t s);
+// top-k over the summed partials (+ logit offset); z_out (nullable) receives z
+hipError_t launch_topk(const double* zpart, int nsplit, const float* logit_bias, double* z_out,
+                       const float* sel_bias, const uint8_t* modality, int n_bias_sets,
+                       int gating, int32_t* idx, float* w, int64_t N, int E, int k,
+                       hipStream_t s);
 
 hipError_t launch_permute(const int32_t* idx, const uint8_t* modality, int32_t* counts,
                           int32_t* mod_counts, int32_t* offsets, int32_t* row_of,

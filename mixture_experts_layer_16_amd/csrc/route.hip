@@ -26,78 +26,112 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 // logits come out within ~1e-7 of their scale of the exact dot product, which
 // keeps the top-k decision equal to the float64 one except for near-ties.
 //
-// Block: 4 waves; tile 64 tokens x 64 experts; wave w owns 16 tokens and the
-// 64 experts (four 16x16 output tiles).  Operands are read straight from global
-// memory (x rows are read once per expert tile, the router matrix stays in L2).
-constexpr int RT_TOK = 64;
+// Block: 4 waves; tile 128 tokens x 64 experts; wave w owns 32 tokens (two
+// 16-row fragments, read straight from global memory) and the block's 64
+// experts, whose 64 x 32 k-slice is staged once per step in LDS (double
+// buffered) for all four waves.  The reduction dimension may be split over
+// gridDim.z blocks (small batches); each split writes float64 partials
+// [split][N][E] and the top-k kernel adds them in split order.
+constexpr int RT_TOK = 128;
 constexpr int RT_EXP = 64;
 
 __global__ __launch_bounds__(256) void router_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-    const float* __restrict__ logit_bias, double* __restrict__ z, int64_t N, int d, int E) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t tok0 = (int64_t)blockIdx.x * RT_TOK + wave * 16;
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, double* __restrict__ zpart,
+    int64_t N, int d, int E, int ksplit_len) {
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][RT_EXP * 32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t tok0 = (int64_t)blockIdx.x * RT_TOK + wave * 32;
   const int e0 = blockIdx.y * RT_EXP;
+  const int k_lo = blockIdx.z * ksplit_len;
+  const int k_hi = min(d, k_lo + ksplit_len);
   const int r16 = lane & 15;     // A row / B column supplied by this lane
   const int kq = lane >> 4;      // which 8-wide k chunk of the 32-wide step
 
-  int64_t arow = tok0 + r16;
-  if (arow >= N) arow = N - 1;
-  const uint16_t* ap = x + arow * (int64_t)d + kq * 8;
-  const uint16_t* bp[4];
+  const uint16_t* ap[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int64_t arow = tok0 + 16 * i + r16;
+    if (arow >= N) arow = N - 1;
+    ap[i] = x + arow * (int64_t)d + kq * 8;
+  }
+  // B staging: thread -> (expert row tid / 4, chunk tid % 4); position of chunk
+  // c of row e in LDS: c ^ ((e >> 2) & 3), conflict-free for the 16-row reads
+  const int se = tid >> 2, sc = tid & 3;
+  int ge = e0 + se;
+  if (ge >= E) ge = E - 1;
+  const uint16_t* bsrc = w + (int64_t)ge * d + sc * 8;
+  const int sdst = se * 32 + ((sc ^ ((se >> 2) & 3)) << 3);
+  int boff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int e = e0 + 16 * j + r16;
-    if (e >= E) e = E - 1;
-    bp[j] = w + (int64_t)e * d + kq * 8;
+    const int e = 16 * j + r16;
+    boff[j] = e * 32 + ((kq ^ ((e >> 2) & 3)) << 3);
   }
 
-  double acc[4][4];
+  double acc[2][4][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[j][v] = 0.0;
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    const bool ok = (k0 + kq * 8) < d;
-    u32x4_t a = {0u, 0u, 0u, 0u};
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  auto ldb = [&](int k0) {
+    return (k0 + sc * 8 < k_hi) ? *reinterpret_cast<const u32x4_t*>(bsrc + k0) : zero;
+  };
+  u32x4_t bnext = ldb(k_lo);
+  *reinterpret_cast<u32x4_t*>(&bs[0][sdst]) = bnext;
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = k_lo; k0 < k_hi; k0 += 32) {
+    const bool more = k0 + 32 < k_hi;
+    if (more) bnext = ldb(k0 + 32);
+    const bool ok = (k0 + kq * 8) < k_hi;
+    u32x4_t a[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = ok ? *reinterpret_cast<const u32x4_t*>(ap[i] + k0) : zero;
     u32x4_t b[4];
-    if (ok) a = *reinterpret_cast<const u32x4_t*>(ap + k0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      b[j] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (ok) b[j] = *reinterpret_cast<const u32x4_t*>(bp[j] + k0);
-    }
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4_t*>(&bs[buf][boff[j]]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[j]), zero4, 0, 0, 0);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[j][v] += (double)p[v];
-    }
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t pp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, b[j]), zero4, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] += (double)pp[v];
+      }
+    if (more) *reinterpret_cast<u32x4_t*>(&bs[buf ^ 1][sdst]) = bnext;
+    __syncthreads();
+    buf ^= 1;
   }
 
   // D layout of the 16x16 output: lane holds column (lane & 15), rows 4*(lane>>4)+v
+  double* zp = zpart + (int64_t)blockIdx.z * N * E;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = e0 + 16 * j + r16;
     if (e >= E) continue;
-    const double ob = logit_bias ? (double)logit_bias[e] : 0.0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t t = tok0 + 4 * kq + v;
-      if (t < N) z[t * E + e] = acc[j][v] + ob;
-    }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t t = tok0 + 16 * i + 4 * kq + v;
+        if (t < N) zp[t * E + e] = acc[i][j][v];
+      }
   }
 }
 
 // fp32 inputs: products of two floats are exact in float64, so the float64
 // FMA chain gives the logits to float64 accuracy.
 __global__ __launch_bounds__(256) void router_f32_kernel(
-    const float* __restrict__ x, const float* __restrict__ w,
-    const float* __restrict__ logit_bias, double* __restrict__ z, int64_t N, int d, int E) {
+    const float* __restrict__ x, const float* __restrict__ w, double* __restrict__ z, int64_t N,
+    int d, int E) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N * E) return;
   const int64_t t = i / E;
@@ -106,7 +140,6 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
   const float* wr = w + (int64_t)e * d;
   double s = 0.0;
   for (int c = 0; c < d; ++c) s = fma((double)xr[c], (double)wr[c], s);
-  if (logit_bias) s += (double)logit_bias[e];
   z[i] = s;
 }
 
@@ -120,15 +153,17 @@ __device__ __forceinline__ bool better(double ka, int ea, double kb, int eb) {
 
 // J = key slots per lane (E <= 64 * J), a compile-time constant so the keys
 // stay in registers.
+// The logits arrive as `nsplit` float64 partial sums [split][N][E]; they are
+// added in split order, plus the logit offset, and optionally written out.
 template <int J>
 __global__ __launch_bounds__(256) void topk_kernel(
-    const double* __restrict__ z, const float* __restrict__ sel_bias,
+    const double* zpart, int nsplit, const float* __restrict__ logit_bias,
+    double* z_out, const float* __restrict__ sel_bias,
     const uint8_t* __restrict__ modality, int n_bias_sets, int gating,
     int32_t* __restrict__ out_idx, float* __restrict__ out_w, int64_t N, int E, int k) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= N) return;
-  const double* zr = z + t * E;
   const int m = (n_bias_sets == 2) ? (int)modality[t] : 0;
   const float* bias = n_bias_sets ? sel_bias + (int64_t)m * E : nullptr;
   const bool sig = (gating == MOE_SIGMOID);
@@ -141,7 +176,10 @@ __global__ __launch_bounds__(256) void topk_kernel(
     key[j] = -INFINITY;
     sc[j] = 0.0;
     if (e < E) {
-      const double zz = zr[e];
+      double zz = zpart[t * E + e];
+      for (int q = 1; q < nsplit; ++q) zz += zpart[((int64_t)q * N + t) * E + e];
+      if (logit_bias) zz += (double)logit_bias[e];
+      if (z_out) z_out[t * E + e] = zz;
       const double s = sig ? 1.0 / (1.0 + exp(-zz)) : zz;   // sigmoid score, or the logit
       double kk = s;
       if (bias) kk += (double)bias[e];
@@ -199,28 +237,49 @@ __global__ __launch_bounds__(256) void topk_kernel(
 
 }  // namespace
 
-hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* w, const float* logit_bias,
-                              double* z, int64_t N, int d, int E, hipStream_t s) {
-  dim3 grid((unsigned)((N + RT_TOK - 1) / RT_TOK), (unsigned)((E + RT_EXP - 1) / RT_EXP));
-  router_bf16_kernel<<<grid, 256, 0, s>>>(x, w, logit_bias, z, N, d, E);
+int router_splits(int64_t N, int d, int E) {
+  const int64_t base = ((N + RT_TOK - 1) / RT_TOK) * ((E + RT_EXP - 1) / RT_EXP);
+  int64_t ks = 512 / (base > 0 ? base : 1);
+  const int64_t kmax = d / 256 > 1 ? d / 256 : 1;
+  if (ks > kmax) ks = kmax;
+  if (ks > kMaxRouterSplits) ks = kMaxRouterSplits;
+  return ks < 1 ? 1 : (int)ks;
+}
+
+hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* w, double* zpart, int nsplit,
+                              int64_t N, int d, int E, hipStream_t s) {
+  // split length: a multiple of 32 covering d in nsplit pieces
+  int len = (d + nsplit - 1) / nsplit;
+  len = (len + 31) / 32 * 32;
+  const int ns = (d + len - 1) / len;
+  dim3 grid((unsigned)((N + RT_TOK - 1) / RT_TOK), (unsigned)((E + RT_EXP - 1) / RT_EXP),
+            (unsigned)ns);
+  router_bf16_kernel<<<grid, 256, 0, s>>>(x, w, zpart, N, d, E, len);
   return hipGetLastError();
 }
 
-hipError_t launch_router_f32(const float* x, const float* w, const float* logit_bias,
-                             double* z, int64_t N, int d, int E, hipStream_t s) {
+int router_splits_used(int d, int nsplit) {
+  int len = (d + nsplit - 1) / nsplit;
+  len = (len + 31) / 32 * 32;
+  return (d + len - 1) / len;
+}
+
+hipError_t launch_router_f32(const float* x, const float* w, double* z, int64_t N, int d, int E,
+                             hipStream_t s) {
   const int64_t n = N * E;
-  router_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, w, logit_bias, z, N, d, E);
+  router_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, w, z, N, d, E);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const double* z, const float* sel_bias, const uint8_t* modality,
-                       int n_bias_sets, int gating, int32_t* idx, float* w, int64_t N,
-                       int E, int k, hipStream_t s) {
+hipError_t launch_topk(const double* zpart, int nsplit, const float* logit_bias, double* z_out,
+                       const float* sel_bias, const uint8_t* modality, int n_bias_sets,
+                       int gating, int32_t* idx, float* w, int64_t N, int E, int k,
+                       hipStream_t s) {
   const unsigned grid = (unsigned)((N + 3) / 4);
   const int J = (E + 63) / 64;
 #define MOE_TOPK(JJ)                                                                        \
-  topk_kernel<JJ><<<grid, 256, 0, s>>>(z, sel_bias, modality, n_bias_sets, gating, idx, w, N, \
-                                       E, k)
+  topk_kernel<JJ><<<grid, 256, 0, s>>>(zpart, nsplit, logit_bias, z_out, sel_bias, modality, \
+                                       n_bias_sets, gating, idx, w, N, E, k)
   if (J <= 1) MOE_TOPK(1);
   else if (J <= 2) MOE_TOPK(2);
   else if (J <= 4) MOE_TOPK(4);

@@ -45,6 +45,9 @@ EDGE = {
     "tail-rows-129": dict(base="cap-s", N=129, f=0.0),
     "no-shared-relu": dict(base="relu-bf16-s", S=0),
     "two-shared": dict(base="ds-s", S=2, N=200),
+    # small batches split the router's reduction over several blocks
+    "split-k-router": dict(base="mixd-s", N=8, d=1024),
+    "split-k-router-ragged": dict(base="ds-s", N=3, d=1000, E=40, k=4),
     "f32-swiglu-clip": dict(base="toy-s", activation="swiglu", clip=0.05, S=1, N=150,
                             toy_draws=False),
     "f32-sigmoid-2bias": dict(base="toy-s", gating="sigmoid", n_bias_sets=2, image_frac=0.3,

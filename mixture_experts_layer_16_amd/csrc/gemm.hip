@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     int base;
-    if (MODE == MODE_GATEUP)   // first half gate rows, second half the matching up rows
+    if constexpr (MODE == MODE_GATEUP)   // first half gate rows, then the matching up rows
       base = (j / (FN / 2)) * CT + wn * WCOLS + 32 * (j % (FN / 2));
     else
       base = wn * WCOLS + 32 * j;

@@ -326,6 +326,67 @@ def forward(x, k: int, E: int, gating: str, activation: str,
 
 
 # ---------------------------------------------------------------------------
+# 5. load-balancing statistics and the aux-loss-free bias update
+
+def expert_load(counts, N: int, k: int) -> np.ndarray:
+    """f_i = count_i / (T k): the share of the batch's assignments that went to
+    expert i; sums to 1 ([Основы] "Практика", ``expert_load``)."""
+    return np.asarray(counts, np.float64) / float(N * k)
+
+
+def mean_router_probs(z: np.ndarray, gating: str) -> np.ndarray:
+    """P_i: the batch mean of the probability the router gives expert i
+    ([Основы] "Вспомогательный лосс Switch Transformer").  Softmax gating: the
+    softmax of the logits.  Sigmoid gating (no softmax on the pages for it):
+    the sigmoid scores normalised over all experts -- a reading."""
+    z = np.asarray(z, np.float64)
+    if z.shape[0] == 0:
+        return np.zeros(z.shape[1])
+    if gating == SOFTMAX:
+        p = softmax(z)
+    else:
+        s = sigmoid(z)
+        p = s / s.sum(axis=-1, keepdims=True)
+    return p.mean(axis=0)
+
+
+def switch_aux(f: np.ndarray, P: np.ndarray, alpha: float = 1.0) -> float:
+    """alpha * N * sum_i f_i P_i with N the number of experts ([Основы]
+    "Вспомогательный лосс Switch Transformer"; 1 when uniform, -> N on
+    collapse)."""
+    f = np.asarray(f, np.float64)
+    return float(alpha * len(f) * np.sum(f * np.asarray(P, np.float64)))
+
+
+def bias_update(bias, counts, n_tokens: int, k: int, gamma: float = 0.001) -> np.ndarray:
+    """Aux-loss-free balancing step: an expert above its target load (n_tokens *
+    k / E assignments) has its selection bias lowered by gamma, one below
+    raised by gamma, one exactly on target left alone ([Groupe] "Le problème
+    de l'équilibre de la charge", "Étape 2"; [V4.1] "L'équilibrage de charge";
+    gamma = 0.001 in [V4.1] "La nouveauté de V4.1").  The comparison is exact
+    (count * E against n_tokens * k in integers); the update is one float32
+    addition, as the biases are float32."""
+    counts = np.asarray(counts, np.int64)
+    E = counts.shape[-1]
+    diff = counts * E - n_tokens * k
+    sgn = np.sign(diff).astype(np.float32)
+    b = np.asarray(bias, np.float32)
+    return (b - np.float32(gamma) * sgn).astype(np.float32)
+
+
+def bias_update_by_modality(bias2, modality_counts, k: int, gamma: float = 0.001) -> np.ndarray:
+    """Two independent bias sets, each updated from its own modality's loads and
+    target N_m k / E ([V4.1] "La nouveauté de V4.1 : l'équilibrage par
+    modalité").  N_m k is the modality's total number of assignments."""
+    mc = np.asarray(modality_counts, np.int64)
+    out = np.empty((2, mc.shape[1]), np.float32)
+    for m in (0, 1):
+        n_m = int(mc[m].sum()) // k
+        out[m] = bias_update(np.asarray(bias2)[m], mc[m], n_m, k, gamma)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # closed forms (parameter counts)
 
 def expert_params(d: int, I: int, activation: str = SWIGLU) -> int:

@@ -225,6 +225,41 @@ int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
                    void* y, const moe_routing* routing_out, const moe_profile* prof,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* Load-balancing statistics of one routed batch and the aux-loss-free bias
+ * update (training-time companion of the forward pass).
+ * Statistics (MoE basics page, "Вспомогательный лосс Switch Transformer"):
+ *   load[e]      = counts[e] / (N k)                 share of assignments
+ *   mean_prob[e] = mean over tokens of p_te          softmax of the logits;
+ *                  for sigmoid gating the token's sigmoid scores divided by
+ *                  their sum
+ *   aux[0]       = E * sum_e load[e] * mean_prob[e]  1 when uniform, E on collapse
+ * (all float64; with N == 0 every statistic is 0).
+ * Update (expert-group lesson, "Le problème de l'équilibre de la charge";
+ * DeepSeek-V4.1 page, "L'équilibrage de charge" and its per-modality
+ * section): for each bias set m, with c = counts (one set) or
+ * modality_counts[m] (two sets) and T_m = sum_e c[e],
+ *   sel_bias[m][e] -= gamma * sign(c[e] * E - T_m)
+ * in float32, the sign decided exactly in integers; on-target experts keep
+ * their bias.
+ *   logits          (device) float64 [N][E]: z as moe_route writes it
+ *                   (needed for mean_prob / aux)
+ *   counts          (device) int32 [E]: demand per expert, as moe_permute
+ *                   writes it (needed for load / aux / one-set update)
+ *   modality_counts (device) int32 [2][E] (needed for a two-set update)
+ *   load, mean_prob (device, nullable) float64 [E] out; aux (device, nullable)
+ *                   float64 [1] out
+ *   sel_bias        (device, nullable) float32 [n_bias_sets][E], updated in
+ *                   place; NULL = no update.  n_bias_sets == 0 with a
+ *                   non-NULL sel_bias is MOE_ERR_INVALID.
+ *   gamma           update rate, finite and >= 0 (else MOE_ERR_INVALID)
+ *   ws, ws_bytes    device workspace (moe_workspace_size is enough); only
+ *                   used for mean_prob / aux.
+ * Results are deterministic (fixed reduction order). */
+int moe_balance(const moe_problem* p, const double* logits, const int32_t* counts,
+                const int32_t* modality_counts, double* load, double* mean_prob,
+                double* aux, float* sel_bias, float gamma, void* ws, size_t ws_bytes,
+                void* stream);
+
 /* Text of a status code (static storage). */
 const char* moe_status_string(int status);
 

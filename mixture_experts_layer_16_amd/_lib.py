@@ -25,7 +25,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_INVALID", -3: "MOE_ERR_U
 # every function include/moe.h declares
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_param_counts", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex",
-           "moe_status_string", "moe_version")
+           "moe_balance", "moe_status_string", "moe_version")
 STAGES = ("route", "permute", "plan", "gate_up", "down", "combine")
 
 
@@ -79,6 +79,7 @@ def _load() -> ctypes.CDLL:
                         ctypes.c_size_t, V],
         "moe_forward_ex": [P, ctypes.POINTER(Weights), V, V, V, V, V, ctypes.POINTER(Routing),
                            ctypes.POINTER(Profile), V, ctypes.c_size_t, V],
+        "moe_balance": [P, V, V, V, V, V, V, V, ctypes.c_float, V, ctypes.c_size_t, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -207,6 +208,17 @@ def moe_combine(p, y_rows, row_of, topk_w, y_shared, y, stream=None, raw=False):
     if raw:
         return st
     _check("moe_combine", st)
+
+
+def moe_balance(p, logits, counts, modality_counts, load, mean_prob, aux, sel_bias, gamma,
+                ws=None, stream=None, raw=False):
+    st = LIB.moe_balance(ctypes.byref(p), ptr(logits), ptr(counts), ptr(modality_counts),
+                         ptr(load), ptr(mean_prob), ptr(aux), ptr(sel_bias), float(gamma),
+                         ptr(ws), ws.numel() if ws is not None and not isinstance(ws, int) else 0,
+                         _stream(stream))
+    if raw:
+        return st
+    _check("moe_balance", st)
 
 
 def weights(w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None) -> Weights:

@@ -40,6 +40,7 @@ WsLayout ws_layout(const moe_problem* p) {
   L.plan = take((3 * (E + S) + 4) * 4);
   L.h = take((nk + N * S) * I * esz);
   L.yrows = take((nk + N * S) * d * esz);
+  L.bal = take((size_t)balance_blocks((int64_t)N) * E * 8);
   L.total = off;
   return L;
 }
@@ -293,6 +294,30 @@ int moe_combine(const moe_problem* p, const void* y_rows, const int32_t* row_of,
   const hipError_t err = launch_combine(p->dtype, y_rows, row_of, topk_w, y_shared,
                                         p->n_tokens, p->n_shared, y, p->n_tokens, p->d_model,
                                         p->top_k, S(stream));
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_balance(const moe_problem* p, const double* logits, const int32_t* counts,
+                const int32_t* modality_counts, double* load, double* mean_prob, double* aux,
+                float* sel_bias, float gamma, void* ws, size_t ws_bytes, void* stream) {
+  const int st = validate(p);
+  if (st) return st;
+  if (!(gamma >= 0.0f) || gamma > 3.0e38f) return MOE_ERR_INVALID;   // rejects NaN too
+  if (sel_bias && p->n_bias_sets == 0) return MOE_ERR_INVALID;
+  if ((mean_prob || aux) && !logits) return MOE_ERR_NULL;
+  if ((load || aux) && !counts) return MOE_ERR_NULL;
+  if (sel_bias && p->n_bias_sets == 1 && !counts) return MOE_ERR_NULL;
+  if (sel_bias && p->n_bias_sets == 2 && !modality_counts) return MOE_ERR_NULL;
+  const size_t need = align256((size_t)balance_blocks(p->n_tokens) * p->n_experts * 8);
+  if (mean_prob || aux) {
+    if (!ws) return MOE_ERR_NULL;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  }
+  if (!load && !mean_prob && !aux && !sel_bias) return MOE_OK;
+  const hipError_t err =
+      launch_balance(logits, counts, modality_counts, static_cast<double*>(ws), load, mean_prob,
+                     aux, sel_bias, p->n_bias_sets, gamma, p->gating, p->n_tokens,
+                     p->n_experts, p->top_k, S(stream));
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -19,8 +19,10 @@ constexpr int kPermTokens = 256;   // tokens per block of the rank kernel
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
-constexpr int kXcds = 8;
-constexpr int kMaxRouterSplits = 32;  // split-K pieces of the router for small batches           // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kMaxRouterSplits = 32;  // split-K pieces of the router for small batches
+constexpr int kBalTokens = 64;        // tokens per block of the balance-statistics kernel
+constexpr int kBalMaxBlocks = 512;    // blocks (and partial rows) of that kernel at most
 
 // ---------------------------------------------------------------------------
 // device workspace layout (byte offsets from the workspace base)
@@ -40,6 +42,7 @@ struct WsLayout {
   size_t plan;          // i32 [3*G+1] tile plan of the grouped GEMMs
   size_t h;             // act [N*k + N*S][I]   expert hidden activations
   size_t yrows;         // act [N*k + N*S][d]   expert outputs per row
+  size_t bal;           // f64 [balance blocks][E] partial probability sums
   size_t total;
 };
 
@@ -105,6 +108,14 @@ struct FfnCall {
   void* marks[6];              // optional hipEvent_t: before/after plan, gate/up, down
 };
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
+
+// Balancing statistics: P_e partial sums per block, then load, P, aux and the
+// optional +-gamma update of the selection biases.
+int64_t balance_blocks(int64_t N);
+hipError_t launch_balance(const double* z, const int32_t* counts, const int32_t* mod_counts,
+                          double* partial, double* load, double* mean_prob, double* aux,
+                          float* sel_bias, int n_bias_sets, float gamma, int gating,
+                          int64_t N, int E, int k, hipStream_t s);
 
 hipError_t launch_combine(int dtype, const void* y_rows, const int32_t* row_of,
                           const float* topk_w, const void* y_shared, int64_t shared_stride_rows,

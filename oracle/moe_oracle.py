@@ -330,8 +330,12 @@ def forward(x, k: int, E: int, gating: str, activation: str,
 
 def expert_load(counts, N: int, k: int) -> np.ndarray:
     """f_i = count_i / (T k): the share of the batch's assignments that went to
-    expert i; sums to 1 ([Основы] "Практика", ``expert_load``)."""
-    return np.asarray(counts, np.float64) / float(N * k)
+    expert i; sums to 1 ([Основы] "Практика", ``expert_load``).  An empty
+    batch has no assignments: every share is 0 there (a reading)."""
+    c = np.asarray(counts, np.float64)
+    if N * k == 0:
+        return np.zeros_like(c)
+    return c / float(N * k)
 
 
 def mean_router_probs(z: np.ndarray, gating: str) -> np.ndarray:

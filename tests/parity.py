@@ -27,6 +27,12 @@ Z_REL_TOL = 5e-7
 W_TOL = 1e-5
 BF16_Y_TOL = 2e-2
 F32_Y_TOL = 1e-4
+# balance statistics from the GPU's own logits: float64 sums of N terms in
+# another order, each term within a few ulps -> |dP| <= 1e-11 (N <= 2^24 would
+# allow ~N*eps = 2e-9 in the worst case; the sums here have N <= 2^16)
+P_ABS_TOL = 1e-11
+AUX_REL_TOL = 1e-12
+GAMMA = 0.001
 
 
 def problem_of(w: synth.Workload, **over):
@@ -202,7 +208,55 @@ def check_layer(ors: OracleSide, y_gpu: torch.Tensor, gidx: np.ndarray, report: 
         assert m <= F32_Y_TOL, report
 
 
-def full_check(w, inp=None, di=None, tokens=None, report=None):
+def check_balance(ors: OracleSide, out: dict, g: dict, di, report: dict, gamma=GAMMA,
+                  ws=None) -> dict:
+    """moe_balance on the GPU's routing outputs against the oracle's balancing
+    statistics: load bit-exact, P from the GPU's own logits within P_ABS_TOL
+    (and from the oracle's logits within the logit tolerance's effect), aux
+    relative AUX_REL_TOL, bias update bit-exact."""
+    w = ors.w
+    N, k, E = w.N, w.k, w.E
+    dev = out["counts"].device
+    p = problem_of(w)
+    load = torch.full((E,), np.nan, dtype=torch.float64, device=dev)
+    prob = torch.full((E,), np.nan, dtype=torch.float64, device=dev)
+    aux = torch.full((1,), np.nan, dtype=torch.float64, device=dev)
+    bias = None if di.sel_bias is None else di.sel_bias.clone()
+    if ws is None:
+        ws = L.workspace(p, dev)
+    L.moe_balance(p, out["logits"], out["counts"], out["modality_counts"], load, prob, aux,
+                  bias, gamma, ws)
+    torch.cuda.synchronize()
+    counts = g["counts"].astype(np.int64)
+    f_ref = O.expert_load(counts, N, k)
+    gl = load.cpu().numpy()
+    assert np.array_equal(gl, f_ref), (gl[:8], f_ref[:8])
+    z = g["logits"][: N * E].reshape(N, E)
+    P_ref = O.mean_router_probs(z, w.gating)
+    gp = prob.cpu().numpy()
+    report["P_abs_err"] = float(np.max(np.abs(gp - P_ref))) if E else 0.0
+    assert report["P_abs_err"] <= P_ABS_TOL, report
+    if N:
+        P_or = O.mean_router_probs(ors.route()["z"], w.gating)
+        report["P_vs_oracle_logits"] = float(np.max(np.abs(gp - P_or)))
+        assert report["P_vs_oracle_logits"] <= 1e-6, report
+    a_ref = O.switch_aux(f_ref, gp)
+    ga = float(aux.cpu().numpy()[0])
+    report["aux"] = ga
+    assert abs(ga - a_ref) <= AUX_REL_TOL * max(abs(a_ref), 1e-300) or (N == 0 and ga == 0.0)
+    if bias is not None:
+        b0 = di.sel_bias.cpu().numpy().reshape(w.n_bias_sets, E)
+        nb = bias.cpu().numpy().reshape(w.n_bias_sets, E)
+        if w.n_bias_sets == 1:
+            ref = O.bias_update(b0[0], counts, N, k, gamma)[None, :]
+        else:
+            ref = O.bias_update_by_modality(b0, g["modality_counts"].reshape(2, E), k, gamma)
+        assert np.array_equal(nb.view(np.uint32), ref.view(np.uint32))
+        report["bias_moved"] = int((nb != b0).sum())
+    return {"load": gl, "P": gp, "aux": ga, "bias": None if bias is None else bias}
+
+
+def full_check(w, inp=None, di=None, tokens=None, report=None, balance=True):
     inp = inp or synth.make_inputs(w)
     di = di or sdev.upload(inp)
     report = {} if report is None else report
@@ -212,4 +266,6 @@ def full_check(w, inp=None, di=None, tokens=None, report=None):
     gidx = check_route(ors, g, report)
     check_dispatch(ors, g, gidx, report)
     check_layer(ors, y, gidx, report, tokens=tokens)
+    if balance:
+        check_balance(ors, out, g, di, report)
     return report, y, g, di

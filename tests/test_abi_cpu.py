@@ -163,3 +163,36 @@ def test_device_entry_points_reject_before_launch(L):
     ws_shared_missing = L.Weights(fake, fake, fake, fake, None, None, None)
     assert lib.moe_forward(ctypes.byref(p), ctypes.byref(ws_shared_missing), fake, None, None,
                            None, fake, None, fake, 1 << 40, None) == -1
+
+
+def test_balance_rejects_before_launch(L):
+    """moe_balance argument checks (host only; nothing is launched)."""
+    fake = 0x10000
+    lib = L.LIB
+    p0 = L.problem(64, 128, 8, 2, 64)                       # no bias sets
+    p1 = L.problem(64, 128, 8, 2, 64, gating="sigmoid", n_bias_sets=1)
+    p2 = L.problem(64, 128, 8, 2, 64, gating="sigmoid", n_bias_sets=2)
+    B = ctypes.byref
+    # a bias update needs bias sets
+    assert lib.moe_balance(B(p0), fake, fake, None, None, None, None, fake, 0.001, fake, 1 << 20,
+                           None) == -2
+    # gamma must be finite and >= 0
+    for g in (-0.001, float("nan"), float("inf")):
+        assert lib.moe_balance(B(p1), fake, fake, None, None, None, None, fake, g, fake, 1 << 20,
+                               None) == -2
+    # P / aux need the logits; load / aux need the counts
+    assert lib.moe_balance(B(p0), None, fake, None, None, fake, None, None, 0.0, fake, 1 << 20,
+                           None) == -1
+    assert lib.moe_balance(B(p0), fake, None, None, fake, None, None, None, 0.0, fake, 1 << 20,
+                           None) == -1
+    # a two-set update needs the per-modality counts
+    assert lib.moe_balance(B(p2), fake, fake, None, None, None, None, fake, 0.001, fake, 1 << 20,
+                           None) == -1
+    # workspace for the probability partials
+    assert lib.moe_balance(B(p0), fake, fake, None, None, fake, None, None, 0.0, None, 0,
+                           None) == -1
+    assert lib.moe_balance(B(p0), fake, fake, None, None, fake, None, None, 0.0, fake, 8,
+                           None) == -4
+    # nothing requested: a no-op
+    assert lib.moe_balance(B(p0), None, None, None, None, None, None, None, 0.0, None, 0,
+                           None) == 0

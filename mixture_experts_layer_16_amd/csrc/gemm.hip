@@ -11,6 +11,8 @@
 // Groups and tiles are planned on the device from the dispatch offsets, so the
 // host never waits for the per-expert row counts: the grid is sized for an upper
 // bound and surplus blocks exit at once.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -93,7 +95,7 @@ __device__ __forceinline__ Tile decode_tile(const int32_t* __restrict__ plan, in
   const int local = L - tile_start[g] * ntn;
   // within a group: super-rows of GM m-tiles; inside one, n-tile major, m-tile
   // minor, so the tiles in flight on one XCD share both x rows and weight rows
-  const int GM = BM >= 256 ? 4 : 8;
+  constexpr int GM = 8;
   const int sr = local / (GM * ntn);
   const int rem = local - sr * GM * ntn;
   const int gm = min(GM, mtg - sr * GM);
@@ -448,6 +450,292 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
 }
 
 // ---------------------------------------------------------------------------
+// bf16 grouped GEMM, direct-to-LDS variant for large groups.
+//
+// Same tile semantics as ffn_gemm_bf16 (C = A B^T over a BM x 256 tile, gate/up
+// pairs, fp16 h and rows), organised for one wave per SIMD:
+//  * four waves in a 2 x 2 layout, each (BM/2) x 128: (BM/64) x 4 accumulators
+//    of 32 x 32, up to 256 fp32 values per lane;
+//  * k-slices of 64 (128-byte rows) go from global memory straight into LDS
+//    with global_load_lds_dwordx4: one wave instruction fills 8 consecutive
+//    rows (1 KiB); each lane picks the global 16-byte chunk whose swizzled
+//    position is its own, so the LDS image equals the swizzled layout without
+//    passing through registers;
+//  * two LDS stages.  The loads of slice kt+2 are issued right after the
+//    barrier that ends slice kt, while the last 16-wide step of slice kt is
+//    still multiplying, and the first fragments of slice kt+1 are read in the
+//    same shadow, so the matrix cores keep running across the barrier.
+// In the down pass the bf16 W_down fragments are converted to fp16 after
+// they are read from LDS (the data never passes through registers before),
+// in the shadow of the preceding step's matrix instructions.
+//
+// One wave instruction: each lane copies 16 bytes from its global address to
+// LDS at lds_base + 16 * lane.  Written as inline assembly so the compiler does
+// not add its conservative wait for every such copy before each LDS read; the
+// kernel waits for them itself (s_waitcnt vmcnt) before the barrier that
+// publishes a stage.  The instruction has no register result.
+__device__ __forceinline__ void g2lds16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// 16 zero bytes in global memory: the source of the copies for k-chunks past
+// the end of a ragged last slice.
+__device__ const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+template <int MODE, int BM>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
+  constexpr int BN = 256, BK = 64;
+  constexpr int ROWS = BM + BN;              // staged rows per slice, 128 bytes each
+  constexpr int NLD = ROWS / 32;             // load instructions per thread per slice
+  constexpr int NLA = BM / 32;               // ... of which for A rows
+  constexpr int WROWS = BM / 2;
+  constexpr int FM = WROWS / 32, FN = 4;
+  constexpr int CT = (MODE == MODE_GATEUP) ? BN / 2 : BN;
+  constexpr int WCOLS = CT / 2;
+  constexpr int SB = ROWS * 128;             // bytes per stage
+  static_assert(BM % 64 == 0 && BM <= 256, "tile rows");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * SB];
+
+  const int ntn = (p.Ncols + CT - 1) / CT;
+  const Tile tl = decode_tile(p.plan, p.G, ntn, BM, CT);
+  if (!tl.ok) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool routed = tl.g < p.n_gather;
+  const char* A = static_cast<const char*>(p.A);
+  const int64_t eoff = (int64_t)(routed ? tl.g : tl.g - p.n_gather) * p.wstride * 2;
+  const char* B0 = static_cast<const char*>(routed ? p.Br0 : p.Bs0) + eoff;
+  const char* B1 = B0;
+  if (MODE == MODE_GATEUP) B1 = static_cast<const char*>(routed ? p.Br1 : p.Bs1) + eoff;
+  const uint32_t lds_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * 1024;
+
+  // ---- loaders: instruction j of wave w fills stage rows R = (4j + w) * 8 ..
+  // R + 7; lane i writes row R + i/8 at position i%8, which holds the global
+  // chunk (i%8) ^ swizzle(row) = (i%8) ^ (i/8) ^ (w & 1).
+  const int lrow = lane >> 3;
+  const int gchunk = (lane & 7) ^ lrow ^ (wave & 1);
+  const char* src[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int r = (4 * j + wave) * 8 + lrow;
+    if (j < NLA) {
+      int m = tl.m0 + r;
+      if (m >= tl.M) m = tl.M - 1;
+      int64_t arow;
+      if (MODE == MODE_DOWN) {
+        arow = tl.rb + m;
+      } else if (routed) {
+        arow = p.token_of_row[tl.rb + m];
+        arow = arow < 0 ? 0 : (arow >= p.n_tokens ? p.n_tokens - 1 : arow);
+      } else {
+        arow = m;
+      }
+      src[j] = A + arow * p.ldA * 2 + gchunk * 16;
+    } else {
+      const int n = r - BM;
+      if (MODE == MODE_GATEUP) {
+        int col = tl.n0 + (n & (CT - 1));
+        if (col >= p.Ncols) col = p.Ncols - 1;
+        src[j] = ((n < CT) ? B0 : B1) + (int64_t)col * p.K * 2 + gchunk * 16;
+      } else {
+        int col = tl.n0 + n;
+        if (col >= p.Ncols) col = p.Ncols - 1;
+        src[j] = B0 + (int64_t)col * p.K * 2 + gchunk * 16;
+      }
+    }
+  }
+  const int nfull = p.K / BK;
+  const int nsl = nfull + ((p.K % BK) ? 1 : 0);   // slices; the last may be ragged
+  // source of copy j of slice kt: in a ragged last slice the chunks at or past
+  // K come from a zero chunk, so the products there vanish
+  auto src_of = [&](int j, int kt) -> const char* {
+    const bool ok = kt < nfull || kt * BK + gchunk * 8 < p.K;
+    return ok ? src[j] + (int64_t)kt * BK * 2 : reinterpret_cast<const char*>(kZeroChunk);
+  };
+  auto issue_slice = [&](int st, int kt) {
+    const uint32_t sb = lds_base + st * SB;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) g2lds16(src_of(j, kt), sb + 4096 * j);
+  };
+
+  // ---- fragment reads: lane supplies row lr of a 32-row fragment and chunk
+  // 2*kk + lh of the slice
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int lsw = (lr & 7) ^ ((lr >> 3) & 1);
+  int a_off[FM], b_off[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) a_off[i] = (wm * WROWS + 32 * i + lr) * 128;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    int base;
+    if constexpr (MODE == MODE_GATEUP)   // gate rows, then the matching up rows
+      base = (j >> 1) * CT + wn * WCOLS + 32 * (j & 1);
+    else
+      base = wn * WCOLS + 32 * j;
+    b_off[j] = (BM + base + lr) * 128;
+  }
+  int kq[BK / 16];
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) kq[kk] = ((2 * kk + lh) ^ lsw) * 16;
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  auto read_frags = [&](int st, int kk, u32x4_t (&af)[FM], u32x4_t (&bf)[FN]) {
+    const char* s = lds + st * SB;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(s + a_off[i] + kq[kk]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const u32x4_t*>(s + b_off[j] + kq[kk]);
+  };
+  // One 16-wide step on fragments (af, bf) with a fixed instruction order:
+  // after MFMA m come the reads 2m and 2m+1 of the next step's fragments (into
+  // na/nb, when RD) and this MFMA's share of the copies of slice dkt into
+  // stage dst (when DMA), so loads and copies issue while the matrix cores
+  // are busy and every fragment read has most of a step to land.
+  auto step = [&](auto RD, auto DMA, const u32x4_t (&af)[FM], const u32x4_t (&bf)[FN], int rst,
+                  int rkk, u32x4_t (&na)[FM], u32x4_t (&nb)[FN], int dst, int dkt) {
+    constexpr bool kRd = decltype(RD)::value, kDma = decltype(DMA)::value;
+    constexpr int NM = FM * FN, NR = FM + FN;
+    const char* rs = lds + rst * SB;
+    const uint32_t sb = lds_base + dst * SB;
+    const u32x4_t (&b)[FN] = bf;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int i = m / FN, j = m % FN;
+      if (MODE == MODE_DOWN)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(f16x8_t, af[i]), __builtin_bit_cast(f16x8_t, b[j]), acc[i][j], 0,
+            0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j],
+            0, 0, 0);
+      if constexpr (kRd) {
+#pragma unroll
+        for (int r = 2 * m; r < 2 * m + 2; ++r) {
+          if (r < FM)
+            na[r] = *reinterpret_cast<const u32x4_t*>(rs + a_off[r] + kq[rkk]);
+          else if (r < NR)
+            nb[r - FM] = *reinterpret_cast<const u32x4_t*>(rs + b_off[r - FM] + kq[rkk]);
+        }
+      }
+      if constexpr (kDma) {
+#pragma unroll
+        for (int d = m * NLD / NM; d < (m + 1) * NLD / NM; ++d) g2lds16(src_of(d, dkt), sb + 4096 * d);
+      }
+      // down pass: the next step's W_down fragments become fp16 in the second
+      // half of the step, once their reads have landed
+      if constexpr (kRd && MODE == MODE_DOWN) {
+        constexpr int H = NM / 2;
+        if (m >= H) {
+#pragma unroll
+          for (int q = (m - H) * 4 * FN / (NM - H); q < (m - H + 1) * 4 * FN / (NM - H); ++q)
+            nb[q / 4][q % 4] = bf16x2_to_f16x2(nb[q / 4][q % 4]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto convert_b = [&](u32x4_t (&bf)[FN]) {
+    if (MODE == MODE_DOWN) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bf[j][q] = bf16x2_to_f16x2(bf[j][q]);
+    }
+  };
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+
+  u32x4_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  issue_slice(0, 0);
+  if (nsl > 1) {
+    issue_slice(1, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");   // slice 0 has landed
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  read_frags(0, 0, fa0, fb0);
+  convert_b(fb0);
+  // Steady state over slices 0 .. nsl-2 (slice kt in stage kt & 1, its step-0
+  // fragments already in fa0/fb0): steps 0-2, then the barrier that both
+  // publishes slice kt+1 and frees stage kt & 1 for slice kt+2, then step 3
+  // of slice kt with the copies of slice kt+2 and the first fragment reads of
+  // slice kt+1 in its shadow.  In the last iteration there is no slice kt+2:
+  // the copies repeat slice nsl-1 into the free stage, which is never read.
+  for (int kt = 0; kt + 1 < nsl; ++kt) {
+    const int st = kt & 1;
+    step(T_{}, F_{}, fa0, fb0, st, 1, fa1, fb1, 0, 0);
+    step(T_{}, F_{}, fa1, fb1, st, 2, fa0, fb0, 0, 0);
+    step(T_{}, F_{}, fa0, fb0, st, 3, fa1, fb1, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    step(T_{}, T_{}, fa1, fb1, st ^ 1, 0, fa0, fb0, st, min(kt + 2, nsl - 1));
+  }
+  {
+    // last slice (stage (nsl-1) & 1)
+    const int st = (nsl - 1) & 1;
+    step(T_{}, F_{}, fa0, fb0, st, 1, fa1, fb1, 0, 0);
+    step(T_{}, F_{}, fa1, fb1, st, 2, fa0, fb0, 0, 0);
+    step(T_{}, F_{}, fa0, fb0, st, 3, fa1, fb1, 0, 0);
+    step(F_{}, F_{}, fa1, fb1, 0, 0, fa0, fb0, 0, 0);
+  }
+  // no copy may still be writing LDS when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue.  32x32 accumulator layout: element v of a lane is row
+  // 8*(v/4) + 4*(lane/32) + v%4, column lane%32.
+  uint16_t* C = static_cast<uint16_t*>(p.C);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = wm * WROWS + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
+      const int m = tl.m0 + row;
+      if (m >= tl.M) continue;
+      uint16_t* crow = C + (tl.rb + m) * p.ldC;
+      if (MODE == MODE_GATEUP) {
+#pragma unroll
+        for (int jn = 0; jn < FN / 2; ++jn) {
+          const int col = tl.n0 + wn * WCOLS + 32 * jn + lr;
+          if (col < p.Ncols) {
+            const float a = acc[i][jn][v];
+            const float u = acc[i][jn + FN / 2][v];
+            float hv = a / (1.0f + __expf(-a)) * u;
+            if (p.clip > 0.f) hv = fminf(fmaxf(hv, -p.clip), p.clip);
+            crow[col] = f32_to_f16_sat(hv);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn) {
+          const int col = tl.n0 + wn * WCOLS + 32 * jn + lr;
+          if (col < p.Ncols) {
+            float vv = acc[i][jn][v];
+            if (MODE == MODE_RELU_UP) vv = fmaxf(vv, 0.f);
+            crow[col] = f32_to_f16_sat(vv);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 grouped GEMM on the vector ALUs (fp32 FMA, fp32 accumulation): the fp32
 // workloads are small and latency-bound.  Tile 64 x 64 outputs, 256 threads with
 // 4 x 4 outputs each (x2 for gate and up), k-slices of 16 through LDS.
@@ -560,15 +848,17 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(GemmParams p) {
 
 struct GemmCfg {
   int bm, bn, bk, wm, wn, minb, nsets, fragdb;
+  int dl;   // 1: ffn_gemm_dl (bm rows x 256, k-slices of 64, 4 waves); other fields unused
 };
 
 // Tile configuration of the bf16 grouped GEMMs for one call (both passes use
 // the same row tiling BM, since they share one tile plan).
-//  * decode-sized groups (at most 32 rows on average): 32-row tiles, so the
-//    matrix cores do not multiply padding rows; the weights stream through LDS
-//    with two slices in flight; the down pass uses 128-wide weight tiles so
-//    enough blocks run when d is small relative to the CU count;
-//  * groups averaging at least 512 rows: 256-row tiles, 8 waves (2 per SIMD);
+//  * batches of at most 64 tokens (decode): 32-row tiles, so the matrix cores
+//    do not multiply padding rows; the weights stream through LDS with two
+//    slices in flight; the down pass uses 128-wide weight tiles so enough
+//    blocks run when d is small relative to the CU count;
+//  * groups averaging at least 128 rows: the direct-to-LDS 256 x 256 kernel,
+//    one wave per SIMD;
 //  * otherwise 128-row tiles, 4 waves, two blocks per CU.
 GemmCfg choose_cfg(const FfnCall& c, int mode) {
 #ifdef MOE_CFG
@@ -580,11 +870,11 @@ GemmCfg choose_cfg(const FfnCall& c, int mode) {
   const int64_t rows = c.routed_rows + c.n_ident * c.N;
   const int64_t avg = groups > 0 ? rows / groups : 0;
   if (c.N <= 64) {
-    if (mode == MODE_DOWN) return GemmCfg{32, 128, 64, 1, 4, 2, 2, 0};
-    return GemmCfg{32, 256, 64, 1, 4, 2, 2, 0};
+    if (mode == MODE_DOWN) return GemmCfg{32, 128, 64, 1, 4, 2, 2, 0, 0};
+    return GemmCfg{32, 256, 64, 1, 4, 2, 2, 0, 0};
   }
-  if (avg >= 512) return GemmCfg{256, 256, 32, 2, 4, 1, 2, 0};
-  return GemmCfg{128, 256, 32, 2, 2, 2, 2, 0};
+  if (avg >= 128) return GemmCfg{256, 256, 64, 2, 2, 1, 0, 0, 1};
+  return GemmCfg{128, 256, 32, 2, 2, 2, 2, 0, 0};
 #endif
 }
 
@@ -611,19 +901,24 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
   int64_t blocks = max_mtiles * ntn;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks <= 0) return hipSuccess;
-  if (dtype == MOE_BF16) {
+  if (dtype == MOE_BF16 && cfg.dl) {
+    if (cfg.bm == 256) ffn_gemm_dl<MODE, 256><<<(unsigned)blocks, 256, 0, s>>>(gp);
+    else if (cfg.bm == 128) ffn_gemm_dl<MODE, 128><<<(unsigned)blocks, 256, 0, s>>>(gp);
+    else return hipErrorInvalidValue;
+  } else if (dtype == MOE_BF16) {
 #define MOE_TRY(a, n, b, c, d, e, f, g)                                                 \
   if (cfg.bm == a && cfg.bn == n && cfg.bk == b && cfg.wm == c && cfg.wn == d &&        \
       cfg.minb == e && cfg.nsets == f && cfg.fragdb == g)                               \
     launch_bf16<MODE, a, n, b, c, d, e, f, g>(gp, blocks, s);                           \
   else
     MOE_TRY(128, 256, 32, 2, 2, 2, 2, 0)
-    MOE_TRY(256, 256, 32, 2, 4, 1, 2, 0)
     MOE_TRY(32, 256, 64, 1, 4, 2, 2, 0)
     MOE_TRY(32, 128, 64, 1, 4, 2, 2, 0)
 #ifdef MOE_CFG
-#define MOE_TRY_CFG(...) MOE_TRY(__VA_ARGS__)
-    MOE_TRY_CFG(MOE_CFG)
+#define MOE_TRY_CFG(a, n, b, c, d, e, f, g, h) MOE_TRY(a, n, b, c, d, e, f, g)
+#define MOE_TRY_CFG2(...) MOE_TRY_CFG(__VA_ARGS__)
+    MOE_TRY_CFG2(MOE_CFG)
+#undef MOE_TRY_CFG2
 #undef MOE_TRY_CFG
 #endif
     return hipErrorInvalidValue;
@@ -649,9 +944,9 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   const int G = c.n_gather + c.n_ident;
   if (G <= 0 || c.N <= 0) return hipSuccess;
   const GemmCfg cfg_up =
-      c.dtype == MOE_BF16 ? choose_cfg(c, MODE_GATEUP) : GemmCfg{kF32BM, kF32BN, 16, 1, 1, 1, 1, 0};
+      c.dtype == MOE_BF16 ? choose_cfg(c, MODE_GATEUP) : GemmCfg{kF32BM, kF32BN, 16, 1, 1, 1, 1, 0, 0};
   const GemmCfg cfg_dn =
-      c.dtype == MOE_BF16 ? choose_cfg(c, MODE_DOWN) : GemmCfg{kF32BM, kF32BN, 16, 1, 1, 1, 1, 0};
+      c.dtype == MOE_BF16 ? choose_cfg(c, MODE_DOWN) : GemmCfg{kF32BM, kF32BN, 16, 1, 1, 1, 1, 0, 0};
   const int bm = cfg_up.bm;
   const int64_t mt = max_mtiles(c, bm);
   const int64_t rows_cap = c.routed_rows;

@@ -485,19 +485,25 @@ __device__ __forceinline__ void g2lds16(const void* src, uint32_t lds_base) {
 // the end of a ragged last slice.
 __device__ const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
 
-template <int MODE, int BM>
+template <int MODE, int BM, int BK, int NS>
 __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
-  constexpr int BN = 256, BK = 64;
-  constexpr int ROWS = BM + BN;              // staged rows per slice, 128 bytes each
-  constexpr int NLD = ROWS / 32;             // load instructions per thread per slice
-  constexpr int NLA = BM / 32;               // ... of which for A rows
+  constexpr int BN = 256;
+  constexpr int KCH = BK / 8;                // 16-byte chunks per staged row
+  constexpr int RPL = 8 / KCH;               // rows per 128-byte LDS line
+  constexpr int KS = BK / 16;                // 16-wide steps per slice
+  constexpr int ROWS = BM + BN;              // staged rows per slice
+  constexpr int LINES = ROWS / RPL;          // 128-byte lines per stage
+  constexpr int NLD = LINES / 32;            // copy instructions per thread per slice
   constexpr int WROWS = BM / 2;
   constexpr int FM = WROWS / 32, FN = 4;
   constexpr int CT = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   constexpr int WCOLS = CT / 2;
-  constexpr int SB = ROWS * 128;             // bytes per stage
+  constexpr int SB = LINES * 128;            // bytes per stage
   static_assert(BM % 64 == 0 && BM <= 256, "tile rows");
-  __shared__ __attribute__((aligned(1024))) char lds[2 * SB];
+  static_assert((BK == 32 || BK == 64) && NS >= 2 && (NS - 1) * NLD <= 63, "pipeline shape");
+  static_assert(KS % 2 == 0, "steps alternate between two fragment sets");
+  static_assert(NS * SB <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[NS * SB];
 
   const int ntn = (p.Ncols + CT - 1) / CT;
   const Tile tl = decode_tile(p.plan, p.G, ntn, BM, CT);
@@ -515,16 +521,24 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
   const uint32_t lds_base =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * 1024;
 
-  // ---- loaders: instruction j of wave w fills stage rows R = (4j + w) * 8 ..
-  // R + 7; lane i writes row R + i/8 at position i%8, which holds the global
-  // chunk (i%8) ^ swizzle(row) = (i%8) ^ (i/8) ^ (w & 1).
-  const int lrow = lane >> 3;
-  const int gchunk = (lane & 7) ^ lrow ^ (wave & 1);
+  // ---- loaders: copy instruction j of wave w fills stage lines (4j + w) * 8
+  // .. + 7; lane i writes line L = (4j + w) * 8 + i/8 at position i%8, which
+  // holds logical chunk c = (i%8) ^ swizzle(L) of the line: row L*RPL + c/KCH,
+  // k-chunk c%KCH.  swizzle(L) depends on i/8 (and for one row per line on w).
+  const int lline = lane >> 3;
+  const int lpos = lane & 7;
+  int gchunk, rsub;
+  {
+    const int sw = (RPL == 1) ? (lline ^ (wave & 1)) : lds_swizzle<2>(lline);
+    const int c = lpos ^ sw;
+    gchunk = c % KCH;
+    rsub = c / KCH;                           // 0 for one row per line
+  }
   const char* src[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
-    const int r = (4 * j + wave) * 8 + lrow;
-    if (j < NLA) {
+    const int r = ((4 * j + wave) * 8 + lline) * RPL + rsub;
+    if (r < BM) {
       int m = tl.m0 + r;
       if (m >= tl.M) m = tl.M - 1;
       int64_t arow;
@@ -564,14 +578,15 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
     for (int j = 0; j < NLD; ++j) g2lds16(src_of(j, kt), sb + 4096 * j);
   };
 
-  // ---- fragment reads: lane supplies row lr of a 32-row fragment and chunk
-  // 2*kk + lh of the slice
+  // ---- fragment reads: lane supplies row lr of a 32-row fragment and k-chunk
+  // 2*kk + lh of the slice; fragment bases are multiples of 32 rows, so the
+  // swizzle of the lane's line depends on lr alone
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 31, lh = lane >> 5;
-  const int lsw = (lr & 7) ^ ((lr >> 3) & 1);
+  const int lsw = lds_swizzle<RPL>(lr / RPL);
   int a_off[FM], b_off[FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) a_off[i] = (wm * WROWS + 32 * i + lr) * 128;
+  for (int i = 0; i < FM; ++i) a_off[i] = ((wm * WROWS + 32 * i + lr) / RPL) * 128;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     int base;
@@ -579,11 +594,11 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
       base = (j >> 1) * CT + wn * WCOLS + 32 * (j & 1);
     else
       base = wn * WCOLS + 32 * j;
-    b_off[j] = (BM + base + lr) * 128;
+    b_off[j] = ((BM + base + lr) / RPL) * 128;
   }
-  int kq[BK / 16];
+  int kq[KS];
 #pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) kq[kk] = ((2 * kk + lh) ^ lsw) * 16;
+  for (int kk = 0; kk < KS; ++kk) kq[kk] = (((lr % RPL) * KCH + 2 * kk + lh) ^ lsw) * 16;
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -661,37 +676,41 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
   using F_ = std::integral_constant<bool, false>;
 
   u32x4_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  issue_slice(0, 0);
-  if (nsl > 1) {
-    issue_slice(1, 1);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");   // slice 0 has landed
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+  // prologue: slices 0 .. NS-1 into stages 0 .. NS-1 (clamped to the last
+  // slice: copies into stages no slice uses are never read); wait for slice 0
+#pragma unroll
+  for (int q = 0; q < NS; ++q) issue_slice(q, min(q, nsl - 1));
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * NLD) : "memory");
   __syncthreads();
   read_frags(0, 0, fa0, fb0);
   convert_b(fb0);
-  // Steady state over slices 0 .. nsl-2 (slice kt in stage kt & 1, its step-0
-  // fragments already in fa0/fb0): steps 0-2, then the barrier that both
-  // publishes slice kt+1 and frees stage kt & 1 for slice kt+2, then step 3
-  // of slice kt with the copies of slice kt+2 and the first fragment reads of
-  // slice kt+1 in its shadow.  In the last iteration there is no slice kt+2:
-  // the copies repeat slice nsl-1 into the free stage, which is never read.
+  // Steady state over slices 0 .. nsl-2 (slice kt in stage kt % NS, its
+  // step-0 fragments already in fa0/fb0).  Steps 0 .. KS-2; then the wait for
+  // slice kt+1 (slices kt+2 .. kt+NS-1 may still fly) and the barrier that
+  // publishes it and frees stage kt % NS; then the last step of slice kt with
+  // the copies of slice kt+NS into the freed stage and the first fragment
+  // reads of slice kt+1 in its shadow.  Copies past the last slice repeat it
+  // into stages that are never read again.
+  int st = 0;
   for (int kt = 0; kt + 1 < nsl; ++kt) {
-    const int st = kt & 1;
-    step(T_{}, F_{}, fa0, fb0, st, 1, fa1, fb1, 0, 0);
-    step(T_{}, F_{}, fa1, fb1, st, 2, fa0, fb0, 0, 0);
-    step(T_{}, F_{}, fa0, fb0, st, 3, fa1, fb1, 0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int nx = (st + 1 == NS) ? 0 : st + 1;
+#pragma unroll
+    for (int kk = 0; kk + 1 < KS; ++kk) {
+      if (kk % 2 == 0) step(T_{}, F_{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+      else step(T_{}, F_{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD) : "memory");
     __syncthreads();
-    step(T_{}, T_{}, fa1, fb1, st ^ 1, 0, fa0, fb0, st, min(kt + 2, nsl - 1));
+    step(T_{}, T_{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + NS, nsl - 1));
+    st = nx;
   }
   {
-    // last slice (stage (nsl-1) & 1)
-    const int st = (nsl - 1) & 1;
-    step(T_{}, F_{}, fa0, fb0, st, 1, fa1, fb1, 0, 0);
-    step(T_{}, F_{}, fa1, fb1, st, 2, fa0, fb0, 0, 0);
-    step(T_{}, F_{}, fa0, fb0, st, 3, fa1, fb1, 0, 0);
+    // last slice (stage st)
+#pragma unroll
+    for (int kk = 0; kk + 1 < KS; ++kk) {
+      if (kk % 2 == 0) step(T_{}, F_{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+      else step(T_{}, F_{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+    }
     step(F_{}, F_{}, fa1, fb1, 0, 0, fa0, fb0, 0, 0);
   }
   // no copy may still be writing LDS when the workgroup ends
@@ -848,7 +867,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(GemmParams p) {
 
 struct GemmCfg {
   int bm, bn, bk, wm, wn, minb, nsets, fragdb;
-  int dl;   // 1: ffn_gemm_dl (bm rows x 256, k-slices of 64, 4 waves); other fields unused
+  int dl;   // 1: ffn_gemm_dl (bm rows x 256, k-slices of bk, nsets LDS stages, 4 waves)
 };
 
 // Tile configuration of the bf16 grouped GEMMs for one call (both passes use
@@ -860,7 +879,13 @@ struct GemmCfg {
 //  * groups averaging at least 128 rows: the direct-to-LDS 256 x 256 kernel,
 //    one wave per SIMD;
 //  * otherwise 128-row tiles, 4 waves, two blocks per CU.
+#ifdef MOE_DLCFG
+static GemmCfg dl_cfg(int bm, int bk, int ns) { return GemmCfg{bm, 256, bk, 2, 2, 1, ns, 0, 1}; }
+#endif
 GemmCfg choose_cfg(const FfnCall& c, int mode) {
+#ifdef MOE_DLCFG
+  if (c.N > 64) return dl_cfg(MOE_DLCFG);
+#endif
 #ifdef MOE_CFG
   (void)c;
   (void)mode;
@@ -873,7 +898,7 @@ GemmCfg choose_cfg(const FfnCall& c, int mode) {
     if (mode == MODE_DOWN) return GemmCfg{32, 128, 64, 1, 4, 2, 2, 0, 0};
     return GemmCfg{32, 256, 64, 1, 4, 2, 2, 0, 0};
   }
-  if (avg >= 128) return GemmCfg{256, 256, 64, 2, 2, 1, 0, 0, 1};
+  if (avg >= 128) return GemmCfg{256, 256, 64, 2, 2, 1, 2, 0, 1};
   return GemmCfg{128, 256, 32, 2, 2, 2, 2, 0, 0};
 #endif
 }
@@ -902,9 +927,16 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks <= 0) return hipSuccess;
   if (dtype == MOE_BF16 && cfg.dl) {
-    if (cfg.bm == 256) ffn_gemm_dl<MODE, 256><<<(unsigned)blocks, 256, 0, s>>>(gp);
-    else if (cfg.bm == 128) ffn_gemm_dl<MODE, 128><<<(unsigned)blocks, 256, 0, s>>>(gp);
-    else return hipErrorInvalidValue;
+#define MOE_DL(a, b, n)                                                   \
+  if (cfg.bm == a && cfg.bk == b && cfg.nsets == n)                       \
+    ffn_gemm_dl<MODE, a, b, n><<<(unsigned)blocks, 256, 0, s>>>(gp);      \
+  else
+    MOE_DL(256, 64, 2)
+    MOE_DL(256, 32, 4)
+    MOE_DL(256, 32, 3)
+    MOE_DL(128, 32, 4)
+    return hipErrorInvalidValue;
+#undef MOE_DL
   } else if (dtype == MOE_BF16) {
 #define MOE_TRY(a, n, b, c, d, e, f, g)                                                 \
   if (cfg.bm == a && cfg.bn == n && cfg.bk == b && cfg.wm == c && cfg.wn == d &&        \

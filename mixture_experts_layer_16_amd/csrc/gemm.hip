@@ -121,6 +121,15 @@ __device__ __forceinline__ int lds_swizzle(int line) {
   return ((line >> 1) & 3) ^ ((line & 1) << 1);
 }
 
+// silu(a) * u, clipped to [-clip, clip] when clip > 0.  The reciprocal is the
+// hardware approximation (about 1 ulp in fp32), far below the fp16 rounding of
+// the stored h.
+__device__ __forceinline__ float swiglu(float a, float u, float clip) {
+  float h = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * u;
+  if (clip > 0.f) h = fminf(fmaxf(h, -clip), clip);
+  return h;
+}
+
 struct GemmParams {
   const void* A;                 // x (gate/up) or h (down)
   const int32_t* token_of_row;   // routed groups of the gate/up pass
@@ -429,9 +438,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
           if (col < p.Ncols) {
             const float a = acc[i][jn][v];
             const float u = acc[i][jn + FN / 2][v];
-            float hv = a / (1.0f + __expf(-a)) * u;
-            if (p.clip > 0.f) hv = fminf(fmaxf(hv, -p.clip), p.clip);
-            crow[col] = f32_to_f16_sat(hv);
+            crow[col] = f32_to_f16_sat(swiglu(a, u, p.clip));
           }
         }
       } else {
@@ -630,13 +637,15 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int i = m / FN, j = m % FN;
+      // weight fragment first: the block of C^T, so each lane ends up with
+      // runs of 4 consecutive output columns of one row
       if (MODE == MODE_DOWN)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(f16x8_t, af[i]), __builtin_bit_cast(f16x8_t, b[j]), acc[i][j], 0,
+            __builtin_bit_cast(f16x8_t, b[j]), __builtin_bit_cast(f16x8_t, af[i]), acc[i][j], 0,
             0, 0);
       else
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j],
+            __builtin_bit_cast(bf16x8_t, b[j]), __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j],
             0, 0, 0);
       if constexpr (kRd) {
 #pragma unroll
@@ -716,39 +725,55 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
   // no copy may still be writing LDS when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue.  32x32 accumulator layout: element v of a lane is row
-  // 8*(v/4) + 4*(lane/32) + v%4, column lane%32.
-  uint16_t* C = static_cast<uint16_t*>(p.C);
+  // ---- epilogue.  acc[i][j] holds the 32 x 32 block of C^T: element v of
+  // lane (lr, lh) is row 32i + lr of the wave's block and column
+  // 8*(v/4) + 4*lh + v%4 of fragment j.  Each lane packs its runs of 4 columns
+  // (fp16) into LDS rows, 64 columns per pass, and the rows leave as 16-byte
+  // stores.
+  __syncthreads();   // every wave is done with the stages (copies were waited for)
+  {
+    constexpr int HC = 64;                       // columns per pass
+    constexpr int PS = HC * 2 + 16;              // LDS row stride in bytes (padded)
+    constexpr int NPASS = (MODE == MODE_GATEUP) ? 1 : 2;
+    constexpr int RDS = WROWS * HC * 2 / 1024;   // 16-byte reads per lane per pass
+    static_assert(4 * WROWS * PS <= NS * SB, "epilogue staging fits the stages");
+    char* eb = lds + wave * (WROWS * PS);
+    uint16_t* C = static_cast<uint16_t*>(p.C);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int pass = 0; pass < NPASS; ++pass) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = wm * WROWS + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
-      const int m = tl.m0 + row;
-      if (m >= tl.M) continue;
-      uint16_t* crow = C + (tl.rb + m) * p.ldC;
-      if (MODE == MODE_GATEUP) {
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int jn = 0; jn < FN / 2; ++jn) {
-          const int col = tl.n0 + wn * WCOLS + 32 * jn + lr;
-          if (col < p.Ncols) {
-            const float a = acc[i][jn][v];
-            const float u = acc[i][jn + FN / 2][v];
-            float hv = a / (1.0f + __expf(-a)) * u;
-            if (p.clip > 0.f) hv = fminf(fmaxf(hv, -p.clip), p.clip);
-            crow[col] = f32_to_f16_sat(hv);
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int vq = 0; vq < 4; ++vq) {
+            float h[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              if (MODE == MODE_GATEUP) {
+                h[c] = swiglu(acc[i][jj][4 * vq + c], acc[i][jj + 2][4 * vq + c], p.clip);
+              } else {
+                h[c] = acc[i][2 * pass + jj][4 * vq + c];
+                if (MODE == MODE_RELU_UP) h[c] = fmaxf(h[c], 0.f);
+              }
+            }
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_f16_sat(h[0]) | ((uint32_t)f32_to_f16_sat(h[1]) << 16);
+            pk.y = (uint32_t)f32_to_f16_sat(h[2]) | ((uint32_t)f32_to_f16_sat(h[3]) << 16);
+            *reinterpret_cast<uint2*>(eb + (32 * i + lr) * PS + (32 * jj + 8 * vq + 4 * lh) * 2) =
+                pk;
           }
-        }
-      } else {
+      // LDS operations of one wave complete in order: the reads below see the
+      // writes above
 #pragma unroll
-        for (int jn = 0; jn < FN; ++jn) {
-          const int col = tl.n0 + wn * WCOLS + 32 * jn + lr;
-          if (col < p.Ncols) {
-            float vv = acc[i][jn][v];
-            if (MODE == MODE_RELU_UP) vv = fmaxf(vv, 0.f);
-            crow[col] = f32_to_f16_sat(vv);
-          }
-        }
+      for (int q = 0; q < RDS; ++q) {
+        const int idx = q * 64 + lane;
+        const int row = idx / (HC / 8), c8 = idx % (HC / 8);
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(eb + row * PS + c8 * 16);
+        const int m = tl.m0 + wm * WROWS + row;
+        const int col = tl.n0 + wn * WCOLS + pass * HC + c8 * 8;
+        if (m < tl.M && col < p.Ncols)
+          *reinterpret_cast<u32x4_t*>(C + (tl.rb + m) * p.ldC + col) = val;
       }
     }
   }

@@ -37,7 +37,7 @@ WsLayout ws_layout(const moe_problem* p) {
   L.drop = take(nk);
   L.lrank = take(nk * 4);
   L.blk_counts = take(nblk * 3 * E * 4);
-  L.plan = take((3 * (E + S) + 4) * 4);
+  L.plan = take(plan_bytes((int)(E + S)));
   L.h = take((nk + N * S) * I * esz);
   L.yrows = take((nk + N * S) * d * esz);
   L.bal = take((size_t)balance_blocks((int64_t)N) * E * 8);
@@ -245,9 +245,9 @@ int moe_expert_ffn(const moe_problem* p, const void* x, const int32_t* token_of_
   const size_t esz = p->dtype == MOE_BF16 ? 2 : 4;
   const int E = p->n_experts;
   const int G = routed ? E : 1;
-  const size_t plan_bytes = align256((size_t)(3 * G + 4) * 4);
+  const size_t plan_sz = align256(plan_bytes(G));
   const size_t rows = routed ? (size_t)N * p->top_k : (size_t)N;
-  const size_t need = plan_bytes + rows * p->d_expert * esz;
+  const size_t need = plan_sz + rows * p->d_expert * esz;
   if (!ws) return MOE_ERR_NULL;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (N == 0) return MOE_OK;
@@ -261,7 +261,7 @@ int moe_expert_ffn(const moe_problem* p, const void* x, const int32_t* token_of_
   c.I = p->d_expert;
   c.x = x;
   c.plan = reinterpret_cast<int32_t*>(base);
-  c.h = base + plan_bytes;
+  c.h = base + plan_sz;
   c.y_rows = y_rows;
   if (routed) {
     c.n_gather = E;

@@ -32,8 +32,10 @@ enum { MODE_GATEUP = 0, MODE_RELU_UP = 1, MODE_DOWN = 2 };
 
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(
     const int32_t* __restrict__ offsets, int n_gather, int n_ident, int64_t N,
-    int64_t rows_cap, int64_t ident_row0, int BM, int32_t* __restrict__ plan) {
+    int64_t rows_cap, int64_t ident_row0, int BM, int BMS, int32_t* __restrict__ plan,
+    int32_t* __restrict__ plan_s) {
   __shared__ int32_t mt[2 * 1024];
+  __shared__ int32_t mts[2 * 1024];
   __shared__ int32_t tmp[1024];
   const int G = n_gather + n_ident;
   int32_t* tile_start = plan;
@@ -53,14 +55,31 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(
       rb = ident_row0 + (int64_t)(g - n_gather) * N;
       r = N;
     }
+    // with a second plan, a remainder of at most BMS rows past the last full
+    // BM-row tile goes to it (one BMS-row tile) instead of a mostly empty
+    // BM-row tile
+    int64_t small = 0;
+    if (plan_s) {
+      const int64_t rem = r % BM;
+      small = (rem > 0 && rem <= BMS) ? rem : 0;
+      plan_s[G + 1 + g] = (int32_t)(rb + r - small);
+      plan_s[G + 1 + G + g] = (int32_t)small;
+      mts[g] = small > 0 ? 1 : 0;
+    }
     row_begin[g] = (int32_t)rb;
-    rows[g] = (int32_t)r;
-    mt[g] = (int32_t)((r + BM - 1) / BM);
+    rows[g] = (int32_t)(r - small);
+    mt[g] = (int32_t)((r - small + BM - 1) / BM);
   }
   __syncthreads();
   const int total = block_exclusive_scan_1024(mt, G, tmp);
   for (int g = threadIdx.x; g < G; g += blockDim.x) tile_start[g] = mt[g];
   if (threadIdx.x == 0) tile_start[G] = total;
+  if (plan_s) {
+    __syncthreads();
+    const int total_s = block_exclusive_scan_1024(mts, G, tmp);
+    for (int g = threadIdx.x; g < G; g += blockDim.x) plan_s[g] = mts[g];
+    if (threadIdx.x == 0) plan_s[G] = total_s;
+  }
 }
 
 struct Tile {
@@ -144,6 +163,8 @@ struct GemmParams {
   int64_t ldA, ldC;              // row strides in elements
   int64_t wstride;               // elements per expert matrix
   int64_t n_tokens;              // clamp for token ids
+  int64_t ident_row0;            // first row of the dense groups (token t of dense
+                                 // group i is row ident_row0 + i*n_tokens + t)
   float clip;
 };
 
@@ -221,7 +242,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
       arow = p.token_of_row[tl.rb + m];
       arow = arow < 0 ? 0 : (arow >= p.n_tokens ? p.n_tokens - 1 : arow);
     } else {
-      arow = m;
+      arow = tl.rb + m - (p.ident_row0 + (int64_t)(tl.g - p.n_gather) * p.n_tokens);
     }
     ag[i] = A + arow * p.ldA + kc * 8;
   }
@@ -555,7 +576,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
         arow = p.token_of_row[tl.rb + m];
         arow = arow < 0 ? 0 : (arow >= p.n_tokens ? p.n_tokens - 1 : arow);
       } else {
-        arow = m;
+        arow = tl.rb + m - (p.ident_row0 + (int64_t)(tl.g - p.n_gather) * p.n_tokens);
       }
       src[j] = A + arow * p.ldA * 2 + gchunk * 16;
     } else {
@@ -629,7 +650,12 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
   // are busy and every fragment read has most of a step to land.
   auto step = [&](auto RD, auto DMA, const u32x4_t (&af)[FM], const u32x4_t (&bf)[FN], int rst,
                   int rkk, u32x4_t (&na)[FM], u32x4_t (&nb)[FN], int dst, int dkt) {
-    constexpr bool kRd = decltype(RD)::value, kDma = decltype(DMA)::value;
+    constexpr bool kRd = decltype(RD)::value;
+    // DMA: 0 none, 1 all copies of slice dkt, 2 its first half, 3 its second half
+    constexpr int kDma = decltype(DMA)::value;
+    constexpr int D0 = (kDma == 3) ? NLD / 2 : 0;
+    constexpr int D1 = (kDma == 2) ? NLD / 2 : NLD;
+    constexpr int ND = kDma ? D1 - D0 : 0;
     constexpr int NM = FM * FN, NR = FM + FN;
     const char* rs = lds + rst * SB;
     const uint32_t sb = lds_base + dst * SB;
@@ -656,9 +682,10 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
             nb[r - FM] = *reinterpret_cast<const u32x4_t*>(rs + b_off[r - FM] + kq[rkk]);
         }
       }
-      if constexpr (kDma) {
+      if constexpr (ND > 0) {
 #pragma unroll
-        for (int d = m * NLD / NM; d < (m + 1) * NLD / NM; ++d) g2lds16(src_of(d, dkt), sb + 4096 * d);
+        for (int d = D0 + m * ND / NM; d < D0 + (m + 1) * ND / NM; ++d)
+          g2lds16(src_of(d, dkt), sb + 4096 * d);
       }
       // down pass: the next step's W_down fragments become fp16 in the second
       // half of the step, once their reads have landed
@@ -683,44 +710,82 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
   };
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
+  using D_NONE = std::integral_constant<int, 0>;
+  using D_ALL = std::integral_constant<int, 1>;
+  using D_LO = std::integral_constant<int, 2>;
+  using D_HI = std::integral_constant<int, 3>;
 
   u32x4_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  // prologue: slices 0 .. NS-1 into stages 0 .. NS-1 (clamped to the last
-  // slice: copies into stages no slice uses are never read); wait for slice 0
-#pragma unroll
-  for (int q = 0; q < NS; ++q) issue_slice(q, min(q, nsl - 1));
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * NLD) : "memory");
-  __syncthreads();
-  read_frags(0, 0, fa0, fb0);
-  convert_b(fb0);
-  // Steady state over slices 0 .. nsl-2 (slice kt in stage kt % NS, its
-  // step-0 fragments already in fa0/fb0).  Steps 0 .. KS-2; then the wait for
-  // slice kt+1 (slices kt+2 .. kt+NS-1 may still fly) and the barrier that
-  // publishes it and frees stage kt % NS; then the last step of slice kt with
-  // the copies of slice kt+NS into the freed stage and the first fragment
-  // reads of slice kt+1 in its shadow.  Copies past the last slice repeat it
-  // into stages that are never read again.
   int st = 0;
-  for (int kt = 0; kt + 1 < nsl; ++kt) {
-    const int nx = (st + 1 == NS) ? 0 : st + 1;
-#pragma unroll
-    for (int kk = 0; kk + 1 < KS; ++kk) {
-      if (kk % 2 == 0) step(T_{}, F_{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
-      else step(T_{}, F_{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
-    }
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD) : "memory");
+  if constexpr (NS == 2) {
+    // prologue: slices 0 and 1 into stages 0 and 1 (clamped to the last slice:
+    // copies into a stage no slice uses are never read); wait for slice 0
+    issue_slice(0, 0);
+    issue_slice(1, min(1, nsl - 1));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
     __syncthreads();
-    step(T_{}, T_{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + NS, nsl - 1));
-    st = nx;
+    read_frags(0, 0, fa0, fb0);
+    convert_b(fb0);
+    // Steady state over slices 0 .. nsl-2 (slice kt in stage kt % 2, its
+    // step-0 fragments already in fa0/fb0).  Steps 0 .. KS-2; then the wait
+    // for slice kt+1 and the barrier that publishes it and frees stage kt % 2;
+    // then the last step of slice kt with the copies of slice kt+2 into the
+    // freed stage and the first fragment reads of slice kt+1 in its shadow.
+    // Copies past the last slice repeat it into a stage never read again.
+    for (int kt = 0; kt + 1 < nsl; ++kt) {
+      const int nx = st ^ 1;
+#pragma unroll
+      for (int kk = 0; kk + 1 < KS; ++kk) {
+        if (kk % 2 == 0) step(T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+        else step(T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      step(T_{}, D_ALL{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + 2, nsl - 1));
+      st = nx;
+    }
+  } else {
+    // Three or more stages: the refill of a stage is spread over two steps so
+    // the copies never queue up in one.  Slice kt+NS goes into stage kt % NS
+    // in two halves: the first in the last step of slice kt (after the
+    // barrier that frees the stage), the second in step 0 of slice kt+1.  At
+    // the end of slice kt, slices kt+2 .. kt+NS-1 (whole) may still be in
+    // flight.  Prologue: slices 0 .. NS-2 and the first half of slice NS-1.
+#pragma unroll
+    for (int q = 0; q + 1 < NS; ++q) issue_slice(q, min(q, nsl - 1));
+    {
+      const uint32_t sb = lds_base + (NS - 1) * SB;
+#pragma unroll
+      for (int j = 0; j < NLD / 2; ++j) g2lds16(src_of(j, min(NS - 1, nsl - 1)), sb + 4096 * j);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD + NLD / 2) : "memory");
+    __syncthreads();
+    read_frags(0, 0, fa0, fb0);
+    convert_b(fb0);
+    int pv = NS - 1;
+    for (int kt = 0; kt + 1 < nsl; ++kt) {
+      const int nx = (st + 1 == NS) ? 0 : st + 1;
+      step(T_{}, D_HI{}, fa0, fb0, st, 1, fa1, fb1, pv, min(kt + NS - 1, nsl - 1));
+#pragma unroll
+      for (int kk = 1; kk + 1 < KS; ++kk) {
+        if (kk % 2 == 0) step(T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+        else step(T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+      }
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD) : "memory");
+      __syncthreads();
+      step(T_{}, D_LO{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + NS, nsl - 1));
+      pv = st;
+      st = nx;
+    }
   }
   {
     // last slice (stage st)
 #pragma unroll
     for (int kk = 0; kk + 1 < KS; ++kk) {
-      if (kk % 2 == 0) step(T_{}, F_{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
-      else step(T_{}, F_{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+      if (kk % 2 == 0) step(T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+      else step(T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
     }
-    step(F_{}, F_{}, fa1, fb1, 0, 0, fa0, fb0, 0, 0);
+    step(F_{}, D_NONE{}, fa1, fb1, 0, 0, fa0, fb0, 0, 0);
   }
   // no copy may still be writing LDS when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -819,7 +884,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(GemmParams p) {
       r = p.token_of_row[tl.rb + m];
       r = r < 0 ? 0 : (r >= p.n_tokens ? p.n_tokens - 1 : r);
     } else {
-      r = m;
+      r = tl.rb + m - (p.ident_row0 + (int64_t)(tl.g - p.n_gather) * p.n_tokens);
     }
     arow[i] = A + r * p.ldA;
     int col = tl.n0 + lrow0 + 16 * i;
@@ -957,9 +1022,9 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
     ffn_gemm_dl<MODE, a, b, n><<<(unsigned)blocks, 256, 0, s>>>(gp);      \
   else
     MOE_DL(256, 64, 2)
+    MOE_DL(128, 64, 2)
     MOE_DL(256, 32, 4)
     MOE_DL(256, 32, 3)
-    MOE_DL(128, 32, 4)
     return hipErrorInvalidValue;
 #undef MOE_DL
   } else if (dtype == MOE_BF16) {
@@ -1005,14 +1070,23 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   const GemmCfg cfg_dn =
       c.dtype == MOE_BF16 ? choose_cfg(c, MODE_DOWN) : GemmCfg{kF32BM, kF32BN, 16, 1, 1, 1, 1, 0, 0};
   const int bm = cfg_up.bm;
+  // 256-row direct-to-LDS tiles: remainders of at most 128 rows run as
+  // 128-row tiles from a second plan, so a group of 300 rows costs one full
+  // and one half tile rather than two full ones.  Only with many groups: the
+  // second launch needs enough remainder tiles to fill the chip (measured:
+  // -3% time with 257 or 385 groups, +8% with 65).
+  const bool split = cfg_up.dl && bm == 256 && cfg_dn.dl && cfg_dn.bm == 256 && G >= 128;
+  const GemmCfg cfg_s{128, 256, 64, 2, 2, 1, 2, 0, 1};
+  int32_t* plan_s = split ? c.plan + plan_stride(G) : nullptr;
   const int64_t mt = max_mtiles(c, bm);
+  const int64_t mt_s = split ? (int64_t)G : 0;
   const int64_t rows_cap = c.routed_rows;
   auto mark = [&](int i) {
     if (c.marks[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(c.marks[i]), s);
   };
   mark(0);
   ffn_plan_kernel<<<1, 1024, 0, s>>>(c.offsets, c.n_gather, c.n_ident, c.N, rows_cap,
-                                     c.identity_row0, bm, c.plan);
+                                     c.identity_row0, bm, 128, c.plan, plan_s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   mark(1);
@@ -1029,15 +1103,24 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   up.ldC = c.I;
   up.wstride = (int64_t)c.I * c.d;
   up.n_tokens = c.N;
+  up.ident_row0 = c.identity_row0;
   up.clip = c.clip;
   up.C = c.h;
-  mark(2);
   if (c.activation == MOE_SWIGLU) {
     up.Br0 = c.wg; up.Br1 = c.wu; up.Bs0 = c.sg; up.Bs1 = c.su;
-    err = launch_gemm<MODE_GATEUP>(up, c.dtype, cfg_up, mt, s);
   } else {
     up.Br0 = c.wu; up.Bs0 = c.su;
-    err = launch_gemm<MODE_RELU_UP>(up, c.dtype, cfg_up, mt, s);
+  }
+  auto gate_up = [&](const GemmParams& gp, const GemmCfg& cfg, int64_t tiles) {
+    return c.activation == MOE_SWIGLU ? launch_gemm<MODE_GATEUP>(gp, c.dtype, cfg, tiles, s)
+                                      : launch_gemm<MODE_RELU_UP>(gp, c.dtype, cfg, tiles, s);
+  };
+  mark(2);
+  err = gate_up(up, cfg_up, mt);
+  if (err == hipSuccess && split) {
+    GemmParams us = up;
+    us.plan = plan_s;
+    err = gate_up(us, cfg_s, mt_s);
   }
   if (err != hipSuccess) return err;
   mark(3);
@@ -1053,11 +1136,17 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   dn.ldC = c.d;
   dn.wstride = (int64_t)c.d * c.I;
   dn.n_tokens = c.N;
+  dn.ident_row0 = c.identity_row0;
   dn.Br0 = c.wd;
   dn.Bs0 = c.sd;
   dn.C = c.y_rows;
   mark(4);
   err = launch_gemm<MODE_DOWN>(dn, c.dtype, cfg_dn, mt, s);
+  if (err == hipSuccess && split) {
+    GemmParams ds = dn;
+    ds.plan = plan_s;
+    err = launch_gemm<MODE_DOWN>(ds, c.dtype, cfg_s, mt_s, s);
+  }
   mark(5);
   return err;
 }

@@ -49,7 +49,11 @@ struct WsLayout {
 WsLayout ws_layout(const moe_problem* p);
 int64_t perm_blocks(int64_t N);
 
-// plan layout: tile_start[G+1], row_begin[G], rows[G]
+// plan layout: tile_start[G+1], row_begin[G], rows[G].  The workspace holds
+// two plans (the second for the remainder tiles of the direct-to-LDS GEMM),
+// plan_stride(G) ints apart.
+inline int64_t plan_stride(int G) { return (3 * (int64_t)G + 1 + 63) / 64 * 64; }
+inline size_t plan_bytes(int G) { return (size_t)(2 * plan_stride(G)) * 4; }
 struct PlanView {
   int32_t* tile_start;
   int32_t* row_begin;

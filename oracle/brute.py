@@ -38,7 +38,8 @@ def best_subset(keys, k):
     return sorted(best, key=lambda i: (-keys[i], i))
 
 
-def route_token(x, w_router, k, gating, logit_bias=None, sel_bias=None, mod=0):
+def route_token(x, w_router, k, gating, logit_bias=None, sel_bias=None, mod=0,
+                renormalize=True):
     E = len(w_router)
     z = [dot(x, w_router[e]) + (logit_bias[e] if logit_bias is not None else 0.0)
          for e in range(E)]
@@ -57,8 +58,11 @@ def route_token(x, w_router, k, gating, logit_bias=None, sel_bias=None, mod=0):
         b = sel_bias[mod] if isinstance(sel_bias[0], (list, tuple)) else sel_bias
         keys = [base[e] + b[e] for e in range(E)]
     chosen = best_subset(keys, k)
-    tot = sum(s[e] for e in chosen)
-    g = [s[e] / tot for e in chosen]
+    if renormalize:
+        tot = sum(s[e] for e in chosen)
+        g = [s[e] / tot for e in chosen]
+    else:                 # the scores themselves (Switch, k = 1: the probability p_i)
+        g = [s[e] for e in chosen]
     return z, chosen, g
 
 
@@ -79,7 +83,7 @@ def ffn(x, wg, wu, wd, activation, clip=0.0):
 
 
 def layer(xs, w_router, experts, shared, k, gating, activation, clip=0.0,
-          C=None, logit_bias=None, sel_bias=None, modality=None):
+          C=None, logit_bias=None, sel_bias=None, modality=None, renormalize=True):
     """Full layer over a tiny batch.  ``experts[e]`` / ``shared[s]`` are
     (wg, wu, wd) nested lists.  Returns (ys, chosen, gates, kept_flags)."""
     E = len(w_router)
@@ -87,7 +91,8 @@ def layer(xs, w_router, experts, shared, k, gating, activation, clip=0.0,
     ys, chosen_all, gates_all, kept_all = [], [], [], []
     for t, x in enumerate(xs):
         mod = modality[t] if modality is not None else 0
-        _, chosen, g = route_token(x, w_router, k, gating, logit_bias, sel_bias, mod)
+        _, chosen, g = route_token(x, w_router, k, gating, logit_bias, sel_bias, mod,
+                                   renormalize)
         y = [0.0] * len(x)
         kept = []
         for e, w in zip(chosen, g):

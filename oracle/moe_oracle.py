@@ -124,14 +124,21 @@ def topk(keys: np.ndarray, k: int) -> np.ndarray:
     return order[:, :k]
 
 
-def gate_weights(s: np.ndarray, idx: np.ndarray) -> np.ndarray:
+def gate_weights(s: np.ndarray, idx: np.ndarray, renormalize: bool = True) -> np.ndarray:
     """Renormalise the chosen (unbiased) scores: g_i = s_i / sum_{j in T} s_j.
 
     [Основы] "Как устроен MoE-слой", step 3; [Routage] "L'idée — Top-k et
     mélange" (0.529, 0.392 -> 0.574, 0.426).  For sigmoid gating the same rule
     applies to the sigmoid scores ([V4.1] "L'équilibrage de charge": combine
-    weights come from the unbiased scores)."""
+    weights come from the unbiased scores).
+
+    ``renormalize=False`` keeps the chosen scores as they are: the Switch
+    Transformer weight with k = 1 is the router probability p_i itself, not 1
+    ([Основы] "Как устроен MoE-слой", paragraph on model variants; the
+    ``MoE.forward`` code in "Эксперимент на PyTorch")."""
     chosen = np.take_along_axis(np.asarray(s, np.float64), idx, axis=-1)
+    if not renormalize:
+        return chosen
     return chosen / chosen.sum(axis=-1, keepdims=True)
 
 
@@ -143,7 +150,8 @@ def softmax_over_chosen(z: np.ndarray, idx: np.ndarray) -> np.ndarray:
 
 
 def route(x, w_router, k: int, gating: str, logit_bias=None, sel_bias=None,
-          modality=None, check_softmax_identity: bool = True) -> dict:
+          modality=None, check_softmax_identity: bool = True,
+          renormalize: bool = True) -> dict:
     """Steps 1-4 of [Основы] "Как устроен MoE-слой" with the selection bias.
 
     Returns z, s (scores), keys, idx [N,k] int64 and g [N,k]."""
@@ -151,8 +159,8 @@ def route(x, w_router, k: int, gating: str, logit_bias=None, sel_bias=None,
     s = scores(z, gating)
     keys = selection_keys(z, s, gating, sel_bias, modality)
     idx = topk(keys, k)
-    g = gate_weights(s, idx)
-    if gating == SOFTMAX and check_softmax_identity and idx.size:
+    g = gate_weights(s, idx, renormalize)
+    if gating == SOFTMAX and renormalize and check_softmax_identity and idx.size:
         alt = softmax_over_chosen(z, idx)
         if not np.allclose(alt, g, rtol=0, atol=1e-12):
             raise AssertionError("renormalised softmax differs from softmax over chosen")
@@ -210,7 +218,11 @@ def dispatch(idx: np.ndarray, E: int, C: Optional[int],
 
     Returns counts [E] (demand, before capacity), modality_counts [2][E] or
     None, offsets [E+1] (prefix sums of kept counts), row_of [N,k] (slot row
-    or -1 when dropped), token_of_row [A], drop_mask [N,k] (uint8)."""
+    or -1 when dropped), token_of_row [A], drop_mask [N,k] (uint8).
+
+    A replayed routing may hold indices outside [0, E): such an assignment
+    goes to no expert, is not counted and is marked dropped (a definition for
+    replay; routing itself never produces one)."""
     idx = np.asarray(idx, np.int64)
     N, k = idx.shape if idx.ndim == 2 else (0, 0)
     counts = np.zeros(E, np.int64)
@@ -246,6 +258,7 @@ def dispatch(idx: np.ndarray, E: int, C: Optional[int],
             sel = idx[mod == m]
             for e in range(E):
                 mod_counts[m, e] = int((sel == e).any(axis=1).sum()) if sel.size else 0
+    drop[(idx < 0) | (idx >= E)] = 1
     return {"counts": counts, "modality_counts": mod_counts, "offsets": offsets,
             "row_of": row_of, "token_of_row": token_of_row, "drop_mask": drop,
             "C": C}
@@ -286,7 +299,8 @@ def forward(x, k: int, E: int, gating: str, activation: str,
             w_router=None, clip: float = 0.0, f: float = 0.0,
             logit_bias=None, sel_bias=None, modality=None,
             forced_idx: Optional[np.ndarray] = None,
-            tokens: Optional[np.ndarray] = None) -> dict:
+            tokens: Optional[np.ndarray] = None, renormalize: bool = True,
+            forced_w: Optional[np.ndarray] = None) -> dict:
     """The whole layer: y_t = sum_{j kept} g_tj FFN_{e_tj}(x_t) + sum_s FFN_s(x_t).
 
     [Основы] "Как устроен MoE-слой", step 4; shared expert and drops:
@@ -294,15 +308,22 @@ def forward(x, k: int, E: int, gating: str, activation: str,
 
     ``get_expert(e)`` returns float64 (w_gate, w_up, w_down) of routed expert e
     (w_gate None for ReLU); ``get_shared(s)`` likewise.  ``forced_idx`` replays
-    a given routing (indices only; weights are recomputed from the scores).
+    a given routing: with ``forced_w`` the weights are taken as given (the
+    router is not evaluated), otherwise they are recomputed from the scores.
     ``tokens`` restricts the output to those token rows (routing and capacity
     are still decided over the whole batch); the result 'y' then has
     len(tokens) rows."""
     x = np.asarray(x, np.float64)
     N = x.shape[0]
-    r = route(x, w_router, k, gating, logit_bias, sel_bias, modality)
-    idx = r["idx"] if forced_idx is None else np.asarray(forced_idx, np.int64)
-    g = gate_weights(r["s"], idx)
+    if forced_w is not None:
+        r = {"z": None, "s": None, "keys": None}
+        idx = np.asarray(forced_idx, np.int64)
+        g = np.asarray(forced_w, np.float64)
+    else:
+        r = route(x, w_router, k, gating, logit_bias, sel_bias, modality,
+                  renormalize=renormalize)
+        idx = r["idx"] if forced_idx is None else np.asarray(forced_idx, np.int64)
+        g = gate_weights(r["s"], np.clip(idx, 0, E - 1), renormalize)
     C = capacity(f, N, k, E)
     disp = dispatch(idx, E, C, modality)
     want = np.arange(N) if tokens is None else np.asarray(tokens, np.int64)

@@ -9,7 +9,7 @@ from oracle import moe_oracle as O
 
 
 def _case(seed, N, d, E, k, I, S, gating, activation, clip=0.0, f=0.0,
-          n_bias_sets=0, logit=False, dup=False):
+          n_bias_sets=0, logit=False, dup=False, renormalize=True):
     rng = np.random.default_rng(seed)
     x = rng.normal(size=(N, d))
     if n_bias_sets == 2:
@@ -28,7 +28,8 @@ def _case(seed, N, d, E, k, I, S, gating, activation, clip=0.0, f=0.0,
     sb = rng.uniform(-0.1, 0.1, size=(n_bias_sets, E)) if n_bias_sets else None
     mod = (rng.random(N) < 0.4).astype(np.uint8) if n_bias_sets == 2 else None
     return dict(x=x, w_router=w_router, W=W, SH=SH, k=k, E=E, gating=gating,
-                activation=activation, clip=clip, f=f, lb=lb, sb=sb, mod=mod)
+                activation=activation, clip=clip, f=f, lb=lb, sb=sb, mod=mod,
+                renormalize=renormalize)
 
 
 CASES = [
@@ -42,6 +43,11 @@ CASES = [
     dict(seed=6, N=11, d=3, E=7, k=1, I=5, S=2, gating="softmax", activation="relu", f=0.5),
     dict(seed=7, N=8, d=4, E=4, k=4, I=3, S=0, gating="sigmoid", activation="swiglu"),
     dict(seed=8, N=12, d=3, E=5, k=2, I=3, S=0, gating="softmax", activation="swiglu", dup=True),
+    # weights without renormalisation: Switch top-1 and a sigmoid top-2
+    dict(seed=9, N=13, d=5, E=6, k=1, I=4, S=1, gating="softmax", activation="swiglu",
+         f=1.0, renormalize=False),
+    dict(seed=10, N=10, d=4, E=6, k=2, I=3, S=0, gating="sigmoid", activation="swiglu",
+         n_bias_sets=1, renormalize=False),
 ]
 
 
@@ -59,12 +65,12 @@ def compare(c, oracle=O):
     ys, chosen, gates, kept = brute.layer(
         xs, c["w_router"].tolist(), experts, shared, c["k"], c["gating"], c["activation"],
         c["clip"], C, None if c["lb"] is None else c["lb"].tolist(), sb,
-        None if c["mod"] is None else c["mod"].tolist())
+        None if c["mod"] is None else c["mod"].tolist(), c["renormalize"])
     out = oracle.forward(c["x"], c["k"], c["E"], c["gating"], c["activation"],
                          get_expert=lambda e: c["W"][e], n_shared=len(c["SH"]),
                          get_shared=lambda s: c["SH"][s], w_router=c["w_router"],
                          clip=c["clip"], f=c["f"], logit_bias=c["lb"], sel_bias=c["sb"],
-                         modality=c["mod"])
+                         modality=c["mod"], renormalize=c["renormalize"])
     same_idx = out["idx"].tolist() == chosen
     dg = float(np.max(np.abs(out["g"] - np.array(gates))))
     same_drop = (out["drop_mask"] == 0).tolist() == kept
@@ -72,7 +78,8 @@ def compare(c, oracle=O):
     return same_idx, dg, same_drop, dy
 
 
-@pytest.mark.parametrize("spec", CASES, ids=lambda s: f"{s['gating']}-{s['activation']}-k{s['k']}-S{s['S']}-{s['seed']}")
+@pytest.mark.parametrize("spec", CASES, ids=lambda s: f"{s['gating']}-{s['activation']}-k{s['k']}-S{s['S']}-{s['seed']}"
+                         + ("" if s.get("renormalize", True) else "-raw"))
 def test_oracle_matches_brute_force(spec):
     c = _case(**spec)
     same_idx, dg, same_drop, dy = compare(c)

@@ -427,3 +427,45 @@ def test_param_counts_trace_and_sparsity():
     c = g["combinations"]
     n = math.comb(c["E"], c["k"])
     assert n == 409_663_695_276_000 and round(n, -14) == c["approx"]
+
+
+def test_switch_top1_weight_is_the_probability():
+    # Switch Transformer: k = 1 and the weight is p_i itself, not renormalised
+    # (Основы MoE, paragraph on model variants).  On the printed logits the
+    # top-1 expert is 0 with p = 0.609; renormalising would give exactly 1.
+    logits = np.array([2.0, 1.0, 0.5, -1.0])
+    x = np.array([[1.0]])
+    w_router = logits[:, None]
+    raw = O.route(x, w_router, 1, "softmax", renormalize=False)
+    ren = O.route(x, w_router, 1, "softmax")
+    assert raw["idx"][0].tolist() == [0] and round(raw["g"][0, 0], 3) == 0.609
+    assert ren["g"][0, 0] == 1.0
+    # raw weights of any k are the scores themselves: with k = E they sum to 1
+    # for softmax, and the sigmoid ones are the sigmoid scores
+    allk = O.route(x, w_router, 4, "softmax", renormalize=False)
+    assert abs(allk["g"].sum() - 1.0) < 1e-15
+    sig = O.route(x, w_router, 2, "sigmoid", renormalize=False)
+    assert np.allclose(sig["g"][0], 1 / (1 + np.exp(-logits[[0, 1]])), rtol=0, atol=1e-15)
+
+
+def test_replay_with_given_weights_and_invalid_indices():
+    # forward(forced_idx, forced_w) uses the given weights as they are; an
+    # index outside [0, E) goes to no expert and is marked dropped
+    rng = np.random.default_rng(3)
+    N, d, E, k, I = 6, 4, 5, 2, 3
+    x = rng.normal(size=(N, d))
+    W = {e: (rng.normal(size=(I, d)), rng.normal(size=(I, d)), rng.normal(size=(d, I)))
+         for e in range(E)}
+    idx = np.array([[0, 1], [2, -1], [4, 3], [1, 7], [3, 2], [0, 4]])
+    gw = rng.uniform(0.1, 1.0, size=(N, k))
+    out = O.forward(x, k, E, "softmax", "swiglu", get_expert=lambda e: W[e],
+                    forced_idx=idx, forced_w=gw)
+    assert out["drop_mask"].tolist() == [[0, 0], [0, 1], [0, 0], [0, 1], [0, 0], [0, 0]]
+    assert out["counts"].tolist() == [2, 2, 2, 2, 2]
+    for t in range(N):
+        ref = np.zeros(d)
+        for j in range(k):
+            e = idx[t, j]
+            if 0 <= e < E:
+                ref += gw[t, j] * O.expert_ffn(x[t:t + 1], *W[e], "swiglu")[0]
+        assert np.max(np.abs(out["y"][t] - ref)) < 1e-12

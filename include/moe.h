@@ -90,7 +90,9 @@ typedef struct {
   int32_t activation;      /* moe_activation */
   int32_t dtype;           /* moe_dtype of x and the weights */
   int32_t n_bias_sets;     /* 0: no selection bias; 1: bias[E]; 2: bias[2][E] by modality */
-  int32_t renormalize;     /* must be 1: gate weights renormalised over the k chosen */
+  int32_t renormalize;     /* 1: gate weights renormalised over the k chosen;
+                              0: the chosen scores as they are (softmax p_i over all
+                              E, or the sigmoid score) -- Switch top-1 style */
   float act_clip;          /* > 0: clamp silu(a)*u to [-act_clip, act_clip]; 0: none */
   double capacity_factor;  /* f > 0: C = ceil(N*k/E * f) (exact); <= 0: unlimited */
 } moe_problem;
@@ -198,6 +200,23 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* x,
                 const float* logit_bias, const float* sel_bias, const uint8_t* modality,
                 void* y, const moe_routing* routing_out, void* ws, size_t ws_bytes,
                 void* stream);
+
+/* Routing replay: the layer with a routing the caller supplies instead of the
+ * router's (permute, routed + shared experts, combine; the MoE basics page,
+ * "Как устроен MoE-слой", step 4, with the dispatch of the routing slides).
+ *   topk_idx (device) int32 [N*k]: expert of each assignment.  Each row should
+ *            hold distinct experts; an index outside [0, E) is an assignment to
+ *            no expert (not counted, marked dropped, contributes nothing).
+ *   topk_w   (device) float32 [N*k]: gate weights, used as given.
+ *   modality (device, nullable) uint8 [N]: only for routing_out->modality_counts.
+ * w->w_router, logit and selection biases are not used.  routing_out (nullable)
+ * receives counts, offsets, row and token maps, drops (its topk_idx, topk_w and
+ * logits are not written).  Capacity applies as in moe_forward.  With the
+ * indices and weights moe_forward produced, y equals its output bit for bit. */
+int moe_forward_routed(const moe_problem* p, const moe_weights* w, const void* x,
+                       const int32_t* topk_idx, const float* topk_w, const uint8_t* modality,
+                       void* y, const moe_routing* routing_out, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Stages of moe_forward, in launch order (indices into moe_profile.ev). */
 enum {

@@ -25,7 +25,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_INVALID", -3: "MOE_ERR_U
 # every function include/moe.h declares
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_param_counts", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex",
-           "moe_balance", "moe_status_string", "moe_version")
+           "moe_balance", "moe_forward_routed", "moe_status_string", "moe_version")
 STAGES = ("route", "permute", "plan", "gate_up", "down", "combine")
 
 
@@ -80,6 +80,8 @@ def _load() -> ctypes.CDLL:
         "moe_forward_ex": [P, ctypes.POINTER(Weights), V, V, V, V, V, ctypes.POINTER(Routing),
                            ctypes.POINTER(Profile), V, ctypes.c_size_t, V],
         "moe_balance": [P, V, V, V, V, V, V, V, ctypes.c_float, V, ctypes.c_size_t, V],
+        "moe_forward_routed": [P, ctypes.POINTER(Weights), V, V, V, V, V,
+                               ctypes.POINTER(Routing), V, ctypes.c_size_t, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -219,6 +221,19 @@ def moe_balance(p, logits, counts, modality_counts, load, mean_prob, aux, sel_bi
     if raw:
         return st
     _check("moe_balance", st)
+
+
+def moe_forward_routed(p, w: "Weights", x, topk_idx, topk_w, modality, y, routing_out=None,
+                       ws=None, stream=None, raw=False):
+    st = LIB.moe_forward_routed(ctypes.byref(p), ctypes.byref(w), ptr(x), ptr(topk_idx),
+                                ptr(topk_w), ptr(modality), ptr(y),
+                                ctypes.byref(routing_out) if routing_out is not None else None,
+                                ptr(ws),
+                                ws.numel() if ws is not None and not isinstance(ws, int) else 0,
+                                _stream(stream))
+    if raw:
+        return st
+    _check("moe_forward_routed", st)
 
 
 def weights(w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None) -> Weights:

@@ -58,7 +58,7 @@ static int validate(const moe_problem* p) {
   if (p->n_bias_sets < 0 || p->n_bias_sets > 2) return MOE_ERR_INVALID;
   if (!(p->act_clip >= 0.0f)) return MOE_ERR_INVALID;             // rejects NaN
   if (isnan(p->capacity_factor)) return MOE_ERR_INVALID;
-  if (p->renormalize != 1) return MOE_ERR_UNSUPPORTED;
+  if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_INVALID;
   if (p->d_model > (1 << 20) || p->d_expert > (1 << 20)) return MOE_ERR_INVALID;
   const int64_t rows = p->n_tokens * (p->top_k + p->n_shared);
   if (rows >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
@@ -128,7 +128,8 @@ static int run_route(const moe_problem* p, const void* x, const void* w_router,
   }
   if (err != hipSuccess) return MOE_ERR_HIP;
   err = launch_topk(zpart, used, logit_bias, z_out, p->n_bias_sets ? sel_bias : nullptr, modality,
-                    p->n_bias_sets, p->gating, idx, w, N, p->n_experts, p->top_k, s);
+                    p->n_bias_sets, p->gating, p->renormalize, idx, w, N, p->n_experts,
+                    p->top_k, s);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -328,15 +329,23 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* x,
                         ws_bytes, stream);
 }
 
-int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
-                   const float* logit_bias, const float* sel_bias, const uint8_t* modality,
-                   void* y, const moe_routing* routing_out, const moe_profile* prof, void* ws,
-                   size_t ws_bytes, void* stream) {
+// The layer after routing (permute, experts, combine) and, unless a routing
+// is given (forced_idx != NULL), the routing itself.
+static int forward_impl(const moe_problem* p, const moe_weights* w, const void* x,
+                        const float* logit_bias, const float* sel_bias,
+                        const uint8_t* modality, void* y, const moe_routing* routing_out,
+                        const moe_profile* prof, void* ws, size_t ws_bytes, void* stream,
+                        const int32_t* forced_idx, const float* forced_w) {
   int st = validate(p);
   if (st) return st;
   if (!w || !y) return MOE_ERR_NULL;
-  st = check_route_inputs(p, x, w->w_router, sel_bias, modality);
-  if (st) return st;
+  if (forced_idx) {
+    if (!forced_w || !x) return MOE_ERR_NULL;
+    if (p->dtype == MOE_BF16 && !aligned16(x)) return MOE_ERR_UNSUPPORTED;
+  } else {
+    st = check_route_inputs(p, x, w->w_router, sel_bias, modality);
+    if (st) return st;
+  }
   if (!w->w_up || !w->w_down) return MOE_ERR_NULL;
   if (p->activation == MOE_SWIGLU && !w->w_gate) return MOE_ERR_NULL;
   if (p->n_shared > 0) {
@@ -360,8 +369,17 @@ int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
   const moe_routing none{};
   const moe_routing& r = routing_out ? *routing_out : none;
   double* zpart = reinterpret_cast<double*>(base + L.logits);
-  int32_t* idx = r.topk_idx ? r.topk_idx : reinterpret_cast<int32_t*>(base + L.topk_idx);
-  float* gw = r.topk_w ? r.topk_w : reinterpret_cast<float*>(base + L.topk_w);
+  const int32_t* idx;
+  const float* gw;
+  if (forced_idx) {
+    idx = forced_idx;
+    gw = forced_w;
+  } else {
+    int32_t* ridx = r.topk_idx ? r.topk_idx : reinterpret_cast<int32_t*>(base + L.topk_idx);
+    float* rw = r.topk_w ? r.topk_w : reinterpret_cast<float*>(base + L.topk_w);
+    idx = ridx;
+    gw = rw;
+  }
   int32_t* counts = r.counts ? r.counts : reinterpret_cast<int32_t*>(base + L.counts);
   int32_t* offsets = r.offsets ? r.offsets : reinterpret_cast<int32_t*>(base + L.offsets);
   int32_t* row_of = r.row_of ? r.row_of : reinterpret_cast<int32_t*>(base + L.row_of);
@@ -373,8 +391,11 @@ int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
     if (prof && prof->ev[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(prof->ev[i]), s);
   };
   mark(2 * MOE_STAGE_ROUTE);
-  st = run_route(p, x, w->w_router, logit_bias, sel_bias, modality, idx, gw, zpart, r.logits, s);
-  if (st) return st;
+  if (!forced_idx) {
+    st = run_route(p, x, w->w_router, logit_bias, sel_bias, modality, const_cast<int32_t*>(idx),
+                   const_cast<float*>(gw), zpart, r.logits, s);
+    if (st) return st;
+  }
   mark(2 * MOE_STAGE_ROUTE + 1);
   mark(2 * MOE_STAGE_PERMUTE);
   if (launch_permute(idx, modality, counts, mcounts, offsets, row_of, tor, drop,
@@ -418,6 +439,23 @@ int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
     return MOE_ERR_HIP;
   mark(2 * MOE_STAGE_COMBINE + 1);
   return MOE_OK;
+}
+
+int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
+                   const float* logit_bias, const float* sel_bias, const uint8_t* modality,
+                   void* y, const moe_routing* routing_out, const moe_profile* prof, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return forward_impl(p, w, x, logit_bias, sel_bias, modality, y, routing_out, prof, ws,
+                      ws_bytes, stream, nullptr, nullptr);
+}
+
+int moe_forward_routed(const moe_problem* p, const moe_weights* w, const void* x,
+                       const int32_t* topk_idx, const float* topk_w, const uint8_t* modality,
+                       void* y, const moe_routing* routing_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!topk_idx || !topk_w) return MOE_ERR_NULL;
+  return forward_impl(p, w, x, nullptr, nullptr, modality, y, routing_out, nullptr, ws,
+                      ws_bytes, stream, topk_idx, topk_w);
 }
 
 const char* moe_status_string(int status) {

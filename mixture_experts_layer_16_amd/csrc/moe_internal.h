@@ -78,8 +78,8 @@ hipError_t launch_router_f32(const float* x, const float* w, double* z, int64_t 
 // top-k over the summed partials (+ logit offset); z_out (nullable) receives z
 hipError_t launch_topk(const double* zpart, int nsplit, const float* logit_bias, double* z_out,
                        const float* sel_bias, const uint8_t* modality, int n_bias_sets,
-                       int gating, int32_t* idx, float* w, int64_t N, int E, int k,
-                       hipStream_t s);
+                       int gating, int renormalize, int32_t* idx, float* w, int64_t N, int E,
+                       int k, hipStream_t s);
 
 hipError_t launch_permute(const int32_t* idx, const uint8_t* modality, int32_t* counts,
                           int32_t* mod_counts, int32_t* offsets, int32_t* row_of,

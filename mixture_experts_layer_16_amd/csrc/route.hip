@@ -159,7 +159,7 @@ template <int J>
 __global__ __launch_bounds__(256) void topk_kernel(
     const double* zpart, int nsplit, const float* __restrict__ logit_bias,
     double* z_out, const float* __restrict__ sel_bias,
-    const uint8_t* __restrict__ modality, int n_bias_sets, int gating,
+    const uint8_t* __restrict__ modality, int n_bias_sets, int gating, int renormalize,
     int32_t* __restrict__ out_idx, float* __restrict__ out_w, int64_t N, int E, int k) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -214,21 +214,43 @@ __global__ __launch_bounds__(256) void topk_kernel(
     if (lane == r) { my_e = be; my_s = ws; }
   }
 
-  // gate weights over the chosen k: softmax over the chosen logits (equal to the
-  // renormalised full softmax), or sigmoid scores divided by their sum.
+  // gate weights.  Renormalised: softmax over the chosen logits (equal to the
+  // renormalised full softmax), or sigmoid scores divided by their sum.  Raw:
+  // the full softmax probability of the chosen expert, or its sigmoid score.
   const bool mine = lane < k;
-  double g;
+  double g, sum;
   if (!sig) {
-    double mx = mine ? my_s : -INFINITY;
+    double mx;
+    if (renormalize) {
+      mx = mine ? my_s : -INFINITY;
+    } else {
+      mx = -INFINITY;                       // max over every expert's logit
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (lane + 64 * j < E) mx = fmax(mx, sc[j]);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
     g = mine ? exp(my_s - mx) : 0.0;
+    if (renormalize) {
+      sum = g;
+    } else {
+      sum = 0.0;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (lane + 64 * j < E) sum += exp(sc[j] - mx);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
   } else {
     g = mine ? my_s : 0.0;
-  }
-  double sum = g;
+    sum = 1.0;
+    if (renormalize) {
+      sum = g;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    }
+  }
   if (mine) {
     out_idx[t * k + lane] = my_e;
     out_w[t * k + lane] = (float)(g / sum);
@@ -273,13 +295,13 @@ hipError_t launch_router_f32(const float* x, const float* w, double* z, int64_t 
 
 hipError_t launch_topk(const double* zpart, int nsplit, const float* logit_bias, double* z_out,
                        const float* sel_bias, const uint8_t* modality, int n_bias_sets,
-                       int gating, int32_t* idx, float* w, int64_t N, int E, int k,
-                       hipStream_t s) {
+                       int gating, int renormalize, int32_t* idx, float* w, int64_t N, int E,
+                       int k, hipStream_t s) {
   const unsigned grid = (unsigned)((N + 3) / 4);
   const int J = (E + 63) / 64;
 #define MOE_TOPK(JJ)                                                                        \
   topk_kernel<JJ><<<grid, 256, 0, s>>>(zpart, nsplit, logit_bias, z_out, sel_bias, modality, \
-                                       n_bias_sets, gating, idx, w, N, E, k)
+                                       n_bias_sets, gating, renormalize, idx, w, N, E, k)
   if (J <= 1) MOE_TOPK(1);
   else if (J <= 2) MOE_TOPK(2);
   else if (J <= 4) MOE_TOPK(4);

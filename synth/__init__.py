@@ -58,6 +58,7 @@ class Workload:
     seed: int = 0
     w_std: float = 0.02
     toy_draws: bool = False      # reproduce the NumPy fiche's draw order (toy layer)
+    renormalize: bool = True     # gate weights renormalised over the k chosen
     notes: str = ""
 
 

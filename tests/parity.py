@@ -37,7 +37,8 @@ GAMMA = 0.001
 
 def problem_of(w: synth.Workload, **over):
     kw = dict(S=w.S, gating=w.gating, activation=w.activation, dtype=w.dtype,
-              n_bias_sets=w.n_bias_sets, act_clip=w.clip, capacity_factor=w.f)
+              n_bias_sets=w.n_bias_sets, act_clip=w.clip, capacity_factor=w.f,
+              renormalize=int(w.renormalize))
     kw.update(over)
     return L.problem(w.N, w.d, w.E, w.k, w.I, **kw)
 
@@ -110,15 +111,17 @@ class OracleSide:
     def route(self):
         if self._route is None:
             w = self.w
-            self._route = O.route(self.x, self.wr, w.k, w.gating, self.lb, self.sb, self.mod)
+            self._route = O.route(self.x, self.wr, w.k, w.gating, self.lb, self.sb, self.mod,
+                                  renormalize=w.renormalize)
         return self._route
 
-    def forward(self, forced_idx, tokens=None):
+    def forward(self, forced_idx, tokens=None, forced_w=None):
         w = self.w
         return O.forward(self.x, w.k, w.E, w.gating, w.activation, get_expert=self.expert,
                          n_shared=w.S, get_shared=self.shared, w_router=self.wr, clip=w.clip,
                          f=w.f, logit_bias=self.lb, sel_bias=self.sb, modality=self.mod,
-                         forced_idx=forced_idx, tokens=tokens)
+                         forced_idx=forced_idx, tokens=tokens, renormalize=w.renormalize,
+                         forced_w=forced_w)
 
 
 def check_route(ors: OracleSide, g: dict, report: dict) -> np.ndarray:
@@ -158,7 +161,8 @@ def check_route(ors: OracleSide, g: dict, report: dict) -> np.ndarray:
         dw = np.abs(np.take_along_axis(gg, perm, 1) - np.take_along_axis(og, operm, 1))
         report["weight_abs_err_max"] = float(dw.max())
         assert report["weight_abs_err_max"] <= W_TOL, report
-        assert float(np.max(np.abs(gw.sum(1) - 1.0))) <= 1e-6
+        if w.renormalize:
+            assert float(np.max(np.abs(gw.sum(1) - 1.0))) <= 1e-6
     # every row holds k distinct experts in range
     assert gidx.min(initial=0) >= 0 and gidx.max(initial=0) < E
     assert all(len(set(row)) == k for row in gidx[: min(N, 2000)].tolist())

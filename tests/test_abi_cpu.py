@@ -101,7 +101,7 @@ BAD = [  # (overrides, expected status)
     (dict(N=-1), -2), (dict(d=0), -2), (dict(I=0), -2), (dict(S=-1), -2), (dict(S=9), -2),
     (dict(gating=5), -2), (dict(activation=3), -2), (dict(dtype=4), -2), (dict(n_bias_sets=3), -2),
     (dict(act_clip=float("nan")), -2), (dict(capacity_factor=float("nan")), -2),
-    (dict(d=100), -3), (dict(I=36), -3), (dict(renormalize=0), -3), (dict(k=33, E=64), -2),
+    (dict(d=100), -3), (dict(I=36), -3), (dict(renormalize=2), -2), (dict(k=33, E=64), -2),
 ]
 
 
@@ -196,3 +196,30 @@ def test_balance_rejects_before_launch(L):
     # nothing requested: a no-op
     assert lib.moe_balance(B(p0), None, None, None, None, None, None, None, 0.0, None, 0,
                            None) == 0
+
+
+def test_raw_weights_are_a_valid_option(L):
+    p = L.problem(64, 128, 8, 1, 64, renormalize=0)
+    assert L.moe_workspace_size(p) > 0
+
+
+def test_forward_routed_rejects_before_launch(L):
+    fake = 0x10000
+    lib = L.LIB
+    p = L.problem(64, 128, 8, 2, 64, S=1)
+    w = L.Weights(None, fake, fake, fake, fake, fake, fake)   # the router is not needed
+    B = ctypes.byref
+    # missing indices or weights
+    assert lib.moe_forward_routed(B(p), B(w), fake, None, fake, None, fake, None, fake,
+                                  1 << 30, None) == -1
+    assert lib.moe_forward_routed(B(p), B(w), fake, fake, None, None, fake, None, fake,
+                                  1 << 30, None) == -1
+    # misaligned bf16 tokens; too small a workspace
+    assert lib.moe_forward_routed(B(p), B(w), fake + 2, fake, fake, None, fake, None, fake,
+                                  1 << 30, None) == -3
+    assert lib.moe_forward_routed(B(p), B(w), fake, fake, fake, None, fake, None, fake, 16,
+                                  None) == -4
+    # shared experts need their weights
+    w2 = L.Weights(None, fake, fake, fake, None, None, None)
+    assert lib.moe_forward_routed(B(p), B(w2), fake, fake, fake, None, fake, None, fake,
+                                  1 << 30, None) == -1

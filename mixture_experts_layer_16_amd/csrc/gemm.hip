@@ -481,18 +481,20 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
 // bf16 grouped GEMM, direct-to-LDS variant for large groups.
 //
 // Same tile semantics as ffn_gemm_bf16 (C = A B^T over a BM x 256 tile, gate/up
-// pairs, fp16 h and rows), organised for one wave per SIMD:
-//  * four waves in a 2 x 2 layout, each (BM/2) x 128: (BM/64) x 4 accumulators
-//    of 32 x 32, up to 256 fp32 values per lane;
-//  * k-slices of 64 (128-byte rows) go from global memory straight into LDS
-//    with global_load_lds_dwordx4: one wave instruction fills 8 consecutive
-//    rows (1 KiB); each lane picks the global 16-byte chunk whose swizzled
-//    position is its own, so the LDS image equals the swizzled layout without
-//    passing through registers;
-//  * two LDS stages.  The loads of slice kt+2 are issued right after the
-//    barrier that ends slice kt, while the last 16-wide step of slice kt is
-//    still multiplying, and the first fragments of slice kt+1 are read in the
-//    same shadow, so the matrix cores keep running across the barrier.
+// pairs, fp16 h and rows):
+//  * NW = 4 waves (one per SIMD) in a 2 x 2 layout, each (BM/2) x 128 with up
+//    to 256 fp32 accumulator values per lane, or NW = 8 waves (two per SIMD)
+//    in a 4 x 2 layout, each (BM/4) x 128, so one wave's copies and reads
+//    issue while the other's MFMAs run;
+//  * k-slices of BK (64: 128-byte rows) go from global memory straight into
+//    LDS with global_load_lds_dwordx4: one wave instruction fills 8
+//    consecutive 128-byte lines (1 KiB); each lane picks the global 16-byte
+//    chunk whose swizzled position is its own, so the LDS image equals the
+//    swizzled layout without passing through registers;
+//  * NS LDS stages.  With two, the loads of slice kt+2 are issued right after
+//    the barrier that ends slice kt, while the last 16-wide step of slice kt
+//    is still multiplying, and the first fragments of slice kt+1 are read in
+//    the same shadow, so the matrix cores keep running across the barrier.
 // In the down pass the bf16 W_down fragments are converted to fp16 after
 // they are read from LDS (the data never passes through registers before),
 // in the shadow of the preceding step's matrix instructions.
@@ -513,21 +515,22 @@ __device__ __forceinline__ void g2lds16(const void* src, uint32_t lds_base) {
 // the end of a ragged last slice.
 __device__ const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
 
-template <int MODE, int BM, int BK, int NS>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
+template <int MODE, int BM, int BK, int NS, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   constexpr int BN = 256;
   constexpr int KCH = BK / 8;                // 16-byte chunks per staged row
   constexpr int RPL = 8 / KCH;               // rows per 128-byte LDS line
   constexpr int KS = BK / 16;                // 16-wide steps per slice
   constexpr int ROWS = BM + BN;              // staged rows per slice
   constexpr int LINES = ROWS / RPL;          // 128-byte lines per stage
-  constexpr int NLD = LINES / 32;            // copy instructions per thread per slice
-  constexpr int WROWS = BM / 2;
+  constexpr int NLD = LINES / (8 * NW);      // copy instructions per thread per slice
+  constexpr int WM = NW / 2;                 // waves along the rows (2 along the columns)
+  constexpr int WROWS = BM / WM;
   constexpr int FM = WROWS / 32, FN = 4;
   constexpr int CT = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   constexpr int WCOLS = CT / 2;
   constexpr int SB = LINES * 128;            // bytes per stage
-  static_assert(BM % 64 == 0 && BM <= 256, "tile rows");
+  static_assert(BM % 64 == 0 && BM <= 256 && (NW == 4 || NW == 8) && WROWS >= 32, "tile rows");
   static_assert((BK == 32 || BK == 64) && NS >= 2 && (NS - 1) * NLD <= 63, "pipeline shape");
   static_assert(KS % 2 == 0, "steps alternate between two fragment sets");
   static_assert(NS * SB <= 160 * 1024, "LDS");
@@ -549,8 +552,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
   const uint32_t lds_base =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * 1024;
 
-  // ---- loaders: copy instruction j of wave w fills stage lines (4j + w) * 8
-  // .. + 7; lane i writes line L = (4j + w) * 8 + i/8 at position i%8, which
+  // ---- loaders: copy instruction j of wave w fills stage lines (NW*j + w) * 8
+  // .. + 7; lane i writes line L = (NW*j + w) * 8 + i/8 at position i%8, which
   // holds logical chunk c = (i%8) ^ swizzle(L) of the line: row L*RPL + c/KCH,
   // k-chunk c%KCH.  swizzle(L) depends on i/8 (and for one row per line on w).
   const int lline = lane >> 3;
@@ -565,7 +568,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
   const char* src[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
-    const int r = ((4 * j + wave) * 8 + lline) * RPL + rsub;
+    const int r = ((NW * j + wave) * 8 + lline) * RPL + rsub;
     if (r < BM) {
       int m = tl.m0 + r;
       if (m >= tl.M) m = tl.M - 1;
@@ -603,13 +606,13 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
   auto issue_slice = [&](int st, int kt) {
     const uint32_t sb = lds_base + st * SB;
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) g2lds16(src_of(j, kt), sb + 4096 * j);
+    for (int j = 0; j < NLD; ++j) g2lds16(src_of(j, kt), sb + NW * 1024 * j);
   };
 
   // ---- fragment reads: lane supplies row lr of a 32-row fragment and k-chunk
   // 2*kk + lh of the slice; fragment bases are multiples of 32 rows, so the
   // swizzle of the lane's line depends on lr alone
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int lr = lane & 31, lh = lane >> 5;
   const int lsw = lds_swizzle<RPL>(lr / RPL);
   int a_off[FM], b_off[FN];
@@ -685,7 +688,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
       if constexpr (ND > 0) {
 #pragma unroll
         for (int d = D0 + m * ND / NM; d < D0 + (m + 1) * ND / NM; ++d)
-          g2lds16(src_of(d, dkt), sb + 4096 * d);
+          g2lds16(src_of(d, dkt), sb + NW * 1024 * d);
       }
       // down pass: the next step's W_down fragments become fp16 in the second
       // half of the step, once their reads have landed
@@ -756,7 +759,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
     {
       const uint32_t sb = lds_base + (NS - 1) * SB;
 #pragma unroll
-      for (int j = 0; j < NLD / 2; ++j) g2lds16(src_of(j, min(NS - 1, nsl - 1)), sb + 4096 * j);
+      for (int j = 0; j < NLD / 2; ++j)
+        g2lds16(src_of(j, min(NS - 1, nsl - 1)), sb + NW * 1024 * j);
     }
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD + NLD / 2) : "memory");
     __syncthreads();
@@ -801,7 +805,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_dl(GemmParams p) {
     constexpr int PS = HC * 2 + 16;              // LDS row stride in bytes (padded)
     constexpr int NPASS = (MODE == MODE_GATEUP) ? 1 : 2;
     constexpr int RDS = WROWS * HC * 2 / 1024;   // 16-byte reads per lane per pass
-    static_assert(4 * WROWS * PS <= NS * SB, "epilogue staging fits the stages");
+    static_assert(NW * WROWS * PS <= NS * SB, "epilogue staging fits the stages");
     char* eb = lds + wave * (WROWS * PS);
     uint16_t* C = static_cast<uint16_t*>(p.C);
 #pragma unroll
@@ -957,7 +961,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(GemmParams p) {
 
 struct GemmCfg {
   int bm, bn, bk, wm, wn, minb, nsets, fragdb;
-  int dl;   // 1: ffn_gemm_dl (bm rows x 256, k-slices of bk, nsets LDS stages, 4 waves)
+  int dl;   // 1: ffn_gemm_dl (bm rows x 256, k-slices of bk, nsets LDS stages, 2*wm waves)
 };
 
 // Tile configuration of the bf16 grouped GEMMs for one call (both passes use
@@ -966,11 +970,13 @@ struct GemmCfg {
 //    do not multiply padding rows; the weights stream through LDS with two
 //    slices in flight; the down pass uses 128-wide weight tiles so enough
 //    blocks run when d is small relative to the CU count;
-//  * groups averaging at least 128 rows: the direct-to-LDS 256 x 256 kernel,
-//    one wave per SIMD;
+//  * groups averaging at least 128 rows: the direct-to-LDS 256 x 256 kernel
+//    (8 waves for gate/up, 4 for down);
 //  * otherwise 128-row tiles, 4 waves, two blocks per CU.
 #ifdef MOE_DLCFG
-static GemmCfg dl_cfg(int bm, int bk, int ns) { return GemmCfg{bm, 256, bk, 2, 2, 1, ns, 0, 1}; }
+static GemmCfg dl_cfg(int bm, int bk, int ns, int nw) {
+  return GemmCfg{bm, 256, bk, nw / 2, 2, 1, ns, 0, 1};
+}
 #endif
 GemmCfg choose_cfg(const FfnCall& c, int mode) {
 #ifdef MOE_DLCFG
@@ -988,7 +994,10 @@ GemmCfg choose_cfg(const FfnCall& c, int mode) {
     if (mode == MODE_DOWN) return GemmCfg{32, 128, 64, 1, 4, 2, 2, 0, 0};
     return GemmCfg{32, 256, 64, 1, 4, 2, 2, 0, 0};
   }
-  if (avg >= 128) return GemmCfg{256, 256, 64, 2, 2, 1, 2, 0, 1};
+  // gate/up with 8 waves (2 per SIMD, 64 x 128 each: one wave's copies hide
+  // behind the other's MFMAs); down with 4 (its per-step fp16 conversion of
+  // W_down fragments is amortised over twice the MFMAs)
+  if (avg >= 128) return GemmCfg{256, 256, 64, mode == MODE_DOWN ? 2 : 4, 2, 1, 2, 0, 1};
   return GemmCfg{128, 256, 32, 2, 2, 2, 2, 0, 0};
 #endif
 }
@@ -1017,14 +1026,14 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks <= 0) return hipSuccess;
   if (dtype == MOE_BF16 && cfg.dl) {
-#define MOE_DL(a, b, n)                                                   \
-  if (cfg.bm == a && cfg.bk == b && cfg.nsets == n)                       \
-    ffn_gemm_dl<MODE, a, b, n><<<(unsigned)blocks, 256, 0, s>>>(gp);      \
+#define MOE_DL(a, b, n, w)                                                        \
+  if (cfg.bm == a && cfg.bk == b && cfg.nsets == n && 2 * cfg.wm == w)            \
+    ffn_gemm_dl<MODE, a, b, n, w><<<(unsigned)blocks, 64 * w, 0, s>>>(gp);       \
   else
-    MOE_DL(256, 64, 2)
-    MOE_DL(128, 64, 2)
-    MOE_DL(256, 32, 4)
-    MOE_DL(256, 32, 3)
+    MOE_DL(256, 64, 2, 4)
+    MOE_DL(128, 64, 2, 4)
+    MOE_DL(256, 64, 2, 8)
+    MOE_DL(256, 32, 3, 8)
     return hipErrorInvalidValue;
 #undef MOE_DL
   } else if (dtype == MOE_BF16) {

@@ -264,6 +264,98 @@ def dispatch(idx: np.ndarray, E: int, C: Optional[int],
             "C": C}
 
 
+def alternates(keys: np.ndarray, k: int) -> np.ndarray:
+    """The experts ranked k+1 .. 2k by key (same order and tie rule as topk);
+    -1 where fewer than 2k experts exist.  int64 [N, k]."""
+    keys = np.asarray(keys, np.float64)
+    N, E = keys.shape
+    order = np.argsort(-keys, axis=-1, kind="stable")
+    alt = np.full((N, k), -1, np.int64)
+    m = max(0, min(k, E - k))
+    alt[:, :m] = order[:, k:k + m]
+    return alt
+
+
+def dispatch_reroute(idx: np.ndarray, alt: np.ndarray, E: int, C: Optional[int]) -> dict:
+    """The overflow policy that hands a dropped assignment to the token's next
+    expert ([Routage] "Politiques de débordement", row "Report sur E2/E3": t6,
+    over capacity at E1, is processed by its third-best expert).
+
+    Reading: first every expert keeps its first C arrivals in token order (the
+    drop dispatch).  Then, walking the assignments in token order (slot order
+    within a token), the q-th dropped slot of token t goes to alt[t, q] -- the
+    token's (k+1+q)-th best expert -- if that expert still has room (C minus
+    its first-round rows minus earlier rerouted rows), else it stays dropped.
+    A rerouted slot keeps its gate weight.  Expert e's rows are its first-round
+    rows (token order) followed by its rerouted rows (token order).
+
+    Returns the drop dispatch's fields with row_of / token_of_row / drop_mask /
+    offsets for the final placement, plus final_idx [N,k] (the expert that
+    processes each slot, -1 if dropped)."""
+    idx = np.asarray(idx, np.int64)
+    alt = np.asarray(alt, np.int64)
+    N, k = idx.shape
+    first = dispatch(idx, E, C)
+    drop1 = first["drop_mask"].astype(bool)
+    kept1 = np.diff(first["offsets"])
+    room = np.zeros(E, np.int64) if C is None else C - kept1
+    taken = np.zeros(E, np.int64)
+    final = np.where(drop1, -1, idx)
+    rank2 = np.full((N, k), -1, np.int64)
+    for t in range(N):
+        q = 0
+        for j in range(k):
+            if not drop1[t, j]:
+                continue
+            c = alt[t, q] if q < k else -1
+            q += 1
+            if C is not None and 0 <= c < E and taken[c] < room[c]:
+                final[t, j] = c
+                rank2[t, j] = taken[c]
+                taken[c] += 1
+    total = kept1 + taken
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(total)
+    row_of = np.full((N, k), -1, np.int64)
+    token_of_row = np.full(int(offsets[E]), -1, np.int64)
+    for t in range(N):
+        for j in range(k):
+            if not drop1[t, j]:
+                e = idx[t, j]
+                r = offsets[e] + (first["row_of"][t, j] - first["offsets"][e])
+            elif rank2[t, j] >= 0:
+                e = final[t, j]
+                r = offsets[e] + kept1[e] + rank2[t, j]
+            else:
+                continue
+            row_of[t, j] = r
+            token_of_row[r] = t
+    out = dict(first)
+    out.update({"offsets": offsets, "row_of": row_of, "token_of_row": token_of_row,
+                "drop_mask": (row_of < 0).astype(np.uint8), "final_idx": final})
+    return out
+
+
+def hash_route(token_ids, E: int, k: int):
+    """A router without parameters ([Groupe] "Exercices", Medium: a
+    deterministic hash-based router).  Reading: h = splitmix64(id) (S. Vigna's
+    published 64-bit mixer: add the golden-ratio increment, then two
+    xor-shift-multiply rounds and a final xor-shift); the token's experts are
+    h mod E, h mod E + 1, ... (mod E) -- k distinct experts -- with equal
+    weights 1/k.  Returns idx [N,k] int64 and g [N,k]."""
+    M = (1 << 64) - 1
+    ids = [int(v) & M for v in np.asarray(token_ids, np.int64).ravel()]
+    idx = np.zeros((len(ids), k), np.int64)
+    for t, v in enumerate(ids):
+        z = (v + 0x9E3779B97F4A7C15) & M
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M
+        z = z ^ (z >> 31)
+        base = z % E
+        idx[t] = [(base + j) % E for j in range(k)]
+    return idx, np.full(idx.shape, 1.0 / k)
+
+
 # ---------------------------------------------------------------------------
 # 4. experts and combine
 

@@ -469,3 +469,104 @@ def test_replay_with_given_weights_and_invalid_indices():
             if 0 <= e < E:
                 ref += gw[t, j] * O.expert_ffn(x[t:t + 1], *W[e], "swiglu")[0]
         assert np.max(np.abs(out["y"][t] - ref)) < 1e-12
+
+
+def test_reroute_policy_on_the_printed_trace():
+    # 'Report sur E2/E3': t6, over capacity at E1 (C = 5), is processed by its
+    # third-best expert instead of being dropped
+    t = gold("routage_trace.json")
+    rr = t["reroute"]
+    idx = np.array(t["assignments"])
+    E, k = t["E"], t["k"]
+    C = O.capacity(t["f"], t["T"], k, E)
+    alt = np.full(idx.shape, -1)
+    alt[rr["token"]] = O.alternates(np.array([rr["t6_logits"]]), k)[0]
+    assert alt[rr["token"], 0] == rr["third_best_expert"]
+    out = O.dispatch_reroute(idx, alt, E, C)
+    assert out["drop_mask"].sum() == 0
+    assert out["final_idx"][rr["token"], rr["slot"]] == rr["third_best_expert"]
+    # the first-round placement is the drop dispatch's, the rerouted row comes
+    # after expert 2's own rows
+    d = O.dispatch(idx, E, C)
+    assert out["counts"].tolist() == t["counts"]
+    e2 = rr["third_best_expert"]
+    kept = np.diff(out["offsets"])
+    assert kept.tolist() == [5, 4, 4, 3]
+    assert out["row_of"][rr["token"], rr["slot"]] == out["offsets"][e2] + 3
+    # slots that were kept keep their order within each expert
+    for e in range(E):
+        a = out["token_of_row"][out["offsets"][e]: out["offsets"][e] + np.diff(d["offsets"])[e]]
+        b = d["token_of_row"][d["offsets"][e]: d["offsets"][e + 1]]
+        assert a.tolist() == b.tolist()
+
+
+def test_reroute_respects_capacity_and_token_order():
+    # brute-force walk over a random case: every expert holds at most C rows,
+    # rerouted slots take the alternates in slot order, earlier tokens first
+    rng = np.random.default_rng(5)
+    N, E, k = 40, 6, 2
+    keys = rng.normal(size=(N, E))
+    keys[:, 0] += 2.0                      # expert 0 overloaded
+    idx = O.topk(keys, k)
+    alt = O.alternates(keys, k)
+    C = O.capacity(1.0, N, k, E)
+    out = O.dispatch_reroute(idx, alt, E, C)
+    assert np.all(np.diff(out["offsets"]) <= C)
+    used = {}
+    first = O.dispatch(idx, E, C)
+    room = {e: C - int(np.diff(first["offsets"])[e]) for e in range(E)}
+    for t in range(N):
+        q = 0
+        for j in range(k):
+            if first["drop_mask"][t, j]:
+                c = alt[t, q]
+                q += 1
+                if used.get(c, 0) < room[c]:
+                    used[c] = used.get(c, 0) + 1
+                    assert out["final_idx"][t, j] == c
+                else:
+                    assert out["final_idx"][t, j] == -1 and out["drop_mask"][t, j] == 1
+            else:
+                assert out["final_idx"][t, j] == idx[t, j]
+    # the alternates are the next keys in order
+    order = np.argsort(-keys, axis=1, kind="stable")
+    assert np.array_equal(alt, order[:, k:2 * k])
+    assert sum(used.values()) > 0
+
+
+def test_hash_router_properties():
+    # the mixer is a bijection of 64-bit words: every step is invertible (odd
+    # multipliers, xor with a right shift), checked by undoing the steps
+    def unmix(z):
+        M = (1 << 64) - 1
+        def unxorshift(y, s):
+            x = y
+            for _ in range(64 // s + 1):
+                x = y ^ (x >> s)
+            return x & M
+        z = unxorshift(z, 31)
+        z = (z * pow(0x94D049BB133111EB, -1, 1 << 64)) & M
+        z = unxorshift(z, 27)
+        z = (z * pow(0xBF58476D1CE4E5B9, -1, 1 << 64)) & M
+        z = unxorshift(z, 30)
+        return (z - 0x9E3779B97F4A7C15) & M
+    ids = np.arange(-50, 5000, 37)
+    E, k = 64, 4
+    idx, g = O.hash_route(ids, E, k)
+    assert np.all(g == 0.25)
+    assert all(len(set(r)) == k for r in idx.tolist())
+    assert np.all(idx[:, 1:] == (idx[:, :1] + np.arange(1, k)) % E)
+    # loads of many ids stay near uniform (binomial bound, 6 sigma)
+    big, _ = O.hash_route(np.arange(200000), E, 1)
+    c = np.bincount(big.ravel(), minlength=E)
+    p = 1 / E
+    assert np.all(np.abs(c - 200000 * p) < 6 * np.sqrt(200000 * p * (1 - p)))
+    # invertibility of the mixer, through the oracle's own expert choice
+    M = (1 << 64) - 1
+    for v in (0, 1, 12345, (1 << 63) - 1):
+        z = (v + 0x9E3779B97F4A7C15) & M
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M
+        z ^= z >> 31
+        assert unmix(z) == v
+        assert O.hash_route([v], E, 1)[0][0, 0] == z % E

@@ -95,7 +95,18 @@ typedef struct {
                               E, or the sigmoid score) -- Switch top-1 style */
   float act_clip;          /* > 0: clamp silu(a)*u to [-act_clip, act_clip]; 0: none */
   double capacity_factor;  /* f > 0: C = ceil(N*k/E * f) (exact); <= 0: unlimited */
+  int32_t overflow;        /* MOE_OVERFLOW_DROP (0) or MOE_OVERFLOW_REROUTE (1) */
 } moe_problem;
+
+/* What happens to an assignment past its expert's capacity (routing slides,
+ * table "Politiques de débordement"): DROP -- it adds nothing (row "Abandon");
+ * REROUTE -- the q-th dropped slot of a token is offered to the token's
+ * (k+1+q)-th best expert (row "Report sur E2/E3"), which accepts offers in
+ * token order while it has room left after its own first-choice rows; an
+ * accepted slot keeps its gate weight, a refused one is dropped.  REROUTE
+ * runs in moe_forward / moe_forward_ex (moe_permute and moe_forward_routed
+ * return MOE_ERR_UNSUPPORTED for it: they have no alternate experts). */
+enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REROUTE = 1 };
 
 /* Expert weights (device).  Routed experts are required; shared ones when S > 0. */
 typedef struct {
@@ -119,6 +130,8 @@ typedef struct {
   int32_t* token_of_row;     /* [N*k] valid in [0, offsets[E]) */
   uint8_t* drop_mask;        /* [N*k] 1 if dropped */
   double* logits;            /* [N][E] router logits z (float64) */
+  int32_t* final_idx;        /* [N*k] expert that processes each slot (the rerouted
+                                one under MOE_OVERFLOW_REROUTE), -1 if dropped */
 } moe_routing;
 
 /* Bytes of device workspace any call below needs for problem p (host). */
@@ -217,6 +230,15 @@ int moe_forward_routed(const moe_problem* p, const moe_weights* w, const void* x
                        const int32_t* topk_idx, const float* topk_w, const uint8_t* modality,
                        void* y, const moe_routing* routing_out, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* A router without parameters (the expert-group lesson's hash-router
+ * exercise, "Exercices", Medium): h = splitmix64(token_ids[t]) (S. Vigna's
+ * 64-bit mixer), experts h mod E, h mod E + 1, ... (mod E), weights 1/k.  Feed
+ * the result to moe_forward_routed.
+ *   token_ids (device) int64 [N]; topk_idx (device) int32 [N*k] out;
+ *   topk_w (device) float32 [N*k] out. */
+int moe_route_hash(const moe_problem* p, const int64_t* token_ids, int32_t* topk_idx,
+                   float* topk_w, void* stream);
 
 /* Stages of moe_forward, in launch order (indices into moe_profile.ev). */
 enum {

@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_OVERFLOW_DROP, MOE_OVERFLOW_REROUTE = 0, 1
 MOE_SWIGLU, MOE_RELU = 0, 1
 MOE_BF16, MOE_F32 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_INVALID", -3: "MOE_ERR_UNSUPPORTED",
@@ -25,7 +26,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_INVALID", -3: "MOE_ERR_U
 # every function include/moe.h declares
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_param_counts", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex",
-           "moe_balance", "moe_forward_routed", "moe_status_string", "moe_version")
+           "moe_balance", "moe_forward_routed", "moe_route_hash", "moe_status_string",
+           "moe_version")
 STAGES = ("route", "permute", "plan", "gate_up", "down", "combine")
 
 
@@ -42,7 +44,7 @@ class Problem(ctypes.Structure):
                 ("gating", ctypes.c_int32), ("activation", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("n_bias_sets", ctypes.c_int32),
                 ("renormalize", ctypes.c_int32), ("act_clip", ctypes.c_float),
-                ("capacity_factor", ctypes.c_double)]
+                ("capacity_factor", ctypes.c_double), ("overflow", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -53,7 +55,7 @@ class Weights(ctypes.Structure):
 class Routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_w", "counts", "modality_counts", "offsets", "row_of",
-                 "token_of_row", "drop_mask", "logits")]
+                 "token_of_row", "drop_mask", "logits", "final_idx")]
 
 
 class Profile(ctypes.Structure):
@@ -82,6 +84,7 @@ def _load() -> ctypes.CDLL:
         "moe_balance": [P, V, V, V, V, V, V, V, ctypes.c_float, V, ctypes.c_size_t, V],
         "moe_forward_routed": [P, ctypes.POINTER(Weights), V, V, V, V, V,
                                ctypes.POINTER(Routing), V, ctypes.c_size_t, V],
+        "moe_route_hash": [P, V, V, V, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -120,16 +123,19 @@ def _stream(stream) -> Optional[int]:
 
 
 def problem(N, d, E, k, I, S=0, gating=MOE_SOFTMAX, activation=MOE_SWIGLU, dtype=MOE_BF16,
-            n_bias_sets=0, act_clip=0.0, capacity_factor=0.0, renormalize=1) -> Problem:
+            n_bias_sets=0, act_clip=0.0, capacity_factor=0.0, renormalize=1,
+            overflow=0) -> Problem:
     if isinstance(gating, str):
         gating = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}[gating]
     if isinstance(activation, str):
         activation = {"swiglu": MOE_SWIGLU, "relu": MOE_RELU}[activation]
     if isinstance(dtype, str):
         dtype = {"bf16": MOE_BF16, "f32": MOE_F32}[dtype]
+    if isinstance(overflow, str):
+        overflow = {"drop": MOE_OVERFLOW_DROP, "reroute": MOE_OVERFLOW_REROUTE}[overflow]
     return Problem(int(N), int(d), int(E), int(k), int(I), int(S), int(gating), int(activation),
                    int(dtype), int(n_bias_sets), int(renormalize), float(act_clip),
-                   float(capacity_factor))
+                   float(capacity_factor), int(overflow))
 
 
 # ---------------------------------------------------------------------------
@@ -234,6 +240,14 @@ def moe_forward_routed(p, w: "Weights", x, topk_idx, topk_w, modality, y, routin
     if raw:
         return st
     _check("moe_forward_routed", st)
+
+
+def moe_route_hash(p, token_ids, topk_idx, topk_w, stream=None, raw=False):
+    st = LIB.moe_route_hash(ctypes.byref(p), ptr(token_ids), ptr(topk_idx), ptr(topk_w),
+                            _stream(stream))
+    if raw:
+        return st
+    _check("moe_route_hash", st)
 
 
 def weights(w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None) -> Weights:

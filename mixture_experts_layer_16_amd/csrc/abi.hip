@@ -41,6 +41,11 @@ WsLayout ws_layout(const moe_problem* p) {
   L.h = take((nk + N * S) * I * esz);
   L.yrows = take((nk + N * S) * d * esz);
   L.bal = take((size_t)balance_blocks((int64_t)N) * E * 8);
+  L.alt = take(nk * 4);
+  L.cand = take(nk * 4);
+  L.lrank2 = take(nk * 4);
+  L.blk2 = take(nblk * 3 * E * 4);
+  L.kept1 = take(E * 4);
   L.total = off;
   return L;
 }
@@ -59,6 +64,8 @@ static int validate(const moe_problem* p) {
   if (!(p->act_clip >= 0.0f)) return MOE_ERR_INVALID;             // rejects NaN
   if (isnan(p->capacity_factor)) return MOE_ERR_INVALID;
   if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_INVALID;
+  if (p->overflow != MOE_OVERFLOW_DROP && p->overflow != MOE_OVERFLOW_REROUTE)
+    return MOE_ERR_INVALID;
   if (p->d_model > (1 << 20) || p->d_expert > (1 << 20)) return MOE_ERR_INVALID;
   const int64_t rows = p->n_tokens * (p->top_k + p->n_shared);
   if (rows >= (int64_t(1) << 31)) return MOE_ERR_INVALID;
@@ -112,7 +119,8 @@ static size_t route_partials_bytes(const moe_problem* p) {
 
 static int run_route(const moe_problem* p, const void* x, const void* w_router,
                      const float* logit_bias, const float* sel_bias, const uint8_t* modality,
-                     int32_t* idx, float* w, double* zpart, double* z_out, hipStream_t s) {
+                     int32_t* idx, float* w, double* zpart, double* z_out, hipStream_t s,
+                     int32_t* alt = nullptr) {
   const int64_t N = p->n_tokens;
   hipError_t err;
   int used = 1;
@@ -128,7 +136,7 @@ static int run_route(const moe_problem* p, const void* x, const void* w_router,
   }
   if (err != hipSuccess) return MOE_ERR_HIP;
   err = launch_topk(zpart, used, logit_bias, z_out, p->n_bias_sets ? sel_bias : nullptr, modality,
-                    p->n_bias_sets, p->gating, p->renormalize, idx, w, N, p->n_experts,
+                    p->n_bias_sets, p->gating, p->renormalize, idx, w, alt, N, p->n_experts,
                     p->top_k, s);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -204,6 +212,7 @@ int moe_permute(const moe_problem* p, const int32_t* topk_idx, const uint8_t* mo
   if (st) return st;
   if (!topk_idx || !counts || !offsets || !row_of || !token_of_row || !drop_mask)
     return MOE_ERR_NULL;
+  if (p->overflow == MOE_OVERFLOW_REROUTE) return MOE_ERR_UNSUPPORTED;
   if (modality_counts && !modality) return MOE_ERR_NULL;
   const int64_t N = p->n_tokens;
   const size_t nk = (size_t)N * p->top_k;
@@ -322,6 +331,18 @@ int moe_balance(const moe_problem* p, const double* logits, const int32_t* count
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int moe_route_hash(const moe_problem* p, const int64_t* token_ids, int32_t* topk_idx,
+                   float* topk_w, void* stream) {
+  const int st = validate(p);
+  if (st) return st;
+  if (!token_ids || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  if (p->n_tokens == 0) return MOE_OK;
+  return launch_hash_route(token_ids, p->n_tokens, p->n_experts, p->top_k, topk_idx, topk_w,
+                           S(stream)) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
 int moe_forward(const moe_problem* p, const moe_weights* w, const void* x,
                 const float* logit_bias, const float* sel_bias, const uint8_t* modality, void* y,
                 const moe_routing* routing_out, void* ws, size_t ws_bytes, void* stream) {
@@ -340,6 +361,7 @@ static int forward_impl(const moe_problem* p, const moe_weights* w, const void* 
   if (st) return st;
   if (!w || !y) return MOE_ERR_NULL;
   if (forced_idx) {
+    if (p->overflow == MOE_OVERFLOW_REROUTE) return MOE_ERR_UNSUPPORTED;
     if (!forced_w || !x) return MOE_ERR_NULL;
     if (p->dtype == MOE_BF16 && !aligned16(x)) return MOE_ERR_UNSUPPORTED;
   } else {
@@ -390,19 +412,33 @@ static int forward_impl(const moe_problem* p, const moe_weights* w, const void* 
   auto mark = [&](int i) {
     if (prof && prof->ev[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(prof->ev[i]), s);
   };
+  const bool reroute = p->overflow == MOE_OVERFLOW_REROUTE;
+  int32_t* alt = reinterpret_cast<int32_t*>(base + L.alt);
   mark(2 * MOE_STAGE_ROUTE);
   if (!forced_idx) {
     st = run_route(p, x, w->w_router, logit_bias, sel_bias, modality, const_cast<int32_t*>(idx),
-                   const_cast<float*>(gw), zpart, r.logits, s);
+                   const_cast<float*>(gw), zpart, r.logits, s, reroute ? alt : nullptr);
     if (st) return st;
   }
   mark(2 * MOE_STAGE_ROUTE + 1);
   mark(2 * MOE_STAGE_PERMUTE);
-  if (launch_permute(idx, modality, counts, mcounts, offsets, row_of, tor, drop,
-                     reinterpret_cast<int32_t*>(base + L.lrank),
-                     reinterpret_cast<int32_t*>(base + L.blk_counts), N, p->n_experts, p->top_k,
-                     capacity_of(p), s) != hipSuccess)
-    return MOE_ERR_HIP;
+  hipError_t perr;
+  if (reroute) {
+    perr = launch_permute_reroute(
+        idx, alt, modality, counts, mcounts, offsets, row_of, tor, drop, r.final_idx,
+        reinterpret_cast<int32_t*>(base + L.lrank), reinterpret_cast<int32_t*>(base + L.blk_counts),
+        reinterpret_cast<int32_t*>(base + L.cand), reinterpret_cast<int32_t*>(base + L.lrank2),
+        reinterpret_cast<int32_t*>(base + L.blk2), reinterpret_cast<int32_t*>(base + L.kept1), N,
+        p->n_experts, p->top_k, capacity_of(p), s);
+  } else {
+    perr = launch_permute(idx, modality, counts, mcounts, offsets, row_of, tor, drop,
+                          reinterpret_cast<int32_t*>(base + L.lrank),
+                          reinterpret_cast<int32_t*>(base + L.blk_counts), N, p->n_experts,
+                          p->top_k, capacity_of(p), s);
+    if (perr == hipSuccess && r.final_idx)
+      perr = launch_final_idx(idx, row_of, r.final_idx, N * p->top_k, s);
+  }
+  if (perr != hipSuccess) return MOE_ERR_HIP;
   mark(2 * MOE_STAGE_PERMUTE + 1);
 
   const size_t esz = p->dtype == MOE_BF16 ? 2 : 4;

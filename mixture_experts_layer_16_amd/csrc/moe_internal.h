@@ -43,6 +43,11 @@ struct WsLayout {
   size_t h;             // act [N*k + N*S][I]   expert hidden activations
   size_t yrows;         // act [N*k + N*S][d]   expert outputs per row
   size_t bal;           // f64 [balance blocks][E] partial probability sums
+  size_t alt;           // i32 [N*k]  alternate experts (reroute policy)
+  size_t cand;          // i32 [N*k]  offered expert of each dropped slot
+  size_t lrank2;        // i32 [N*k]  block-local ranks of the offers
+  size_t blk2;          // i32 [nblk][3][E] per-block offers, then bases
+  size_t kept1;         // i32 [E]    first-round rows per expert
   size_t total;
 };
 
@@ -76,16 +81,33 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* w, double* zpar
 hipError_t launch_router_f32(const float* x, const float* w, double* z, int64_t N, int d, int E,
                              hipStream_t s);
 // top-k over the summed partials (+ logit offset); z_out (nullable) receives z
+// alt (nullable) [N*k]: the experts ranked k+1 .. 2k, -1 past E
 hipError_t launch_topk(const double* zpart, int nsplit, const float* logit_bias, double* z_out,
                        const float* sel_bias, const uint8_t* modality, int n_bias_sets,
-                       int gating, int renormalize, int32_t* idx, float* w, int64_t N, int E,
-                       int k, hipStream_t s);
+                       int gating, int renormalize, int32_t* idx, float* w, int32_t* alt,
+                       int64_t N, int E, int k, hipStream_t s);
+hipError_t launch_hash_route(const int64_t* ids, int64_t N, int E, int k, int32_t* idx,
+                             float* w, hipStream_t s);
 
 hipError_t launch_permute(const int32_t* idx, const uint8_t* modality, int32_t* counts,
                           int32_t* mod_counts, int32_t* offsets, int32_t* row_of,
                           int32_t* token_of_row, uint8_t* drop, int32_t* lrank,
                           int32_t* blk_counts, int64_t N, int E, int k, int64_t C,
                           hipStream_t s);
+// final_idx[a] = idx[a] if row_of[a] >= 0 else -1 (the drop policy's final experts)
+hipError_t launch_final_idx(const int32_t* idx, const int32_t* row_of, int32_t* final_idx,
+                            int64_t nk, hipStream_t s);
+// Reroute policy: as launch_permute, then the q-th dropped slot of a token goes
+// to alt[t*k+q] if that expert has room; final_idx (nullable) gets the expert
+// that processes each slot (-1 if dropped).  Scratch: cand, lrank2 [N*k],
+// blk2 [nblk][3][E], kept1 [E].
+hipError_t launch_permute_reroute(const int32_t* idx, const int32_t* alt,
+                                  const uint8_t* modality, int32_t* counts,
+                                  int32_t* mod_counts, int32_t* offsets, int32_t* row_of,
+                                  int32_t* token_of_row, uint8_t* drop, int32_t* final_idx,
+                                  int32_t* lrank, int32_t* blk_counts, int32_t* cand,
+                                  int32_t* lrank2, int32_t* blk2, int32_t* kept1, int64_t N,
+                                  int E, int k, int64_t C, hipStream_t s);
 
 // Grouped FFN over G groups.  Groups [0, n_gather) are routed experts whose
 // rows come from `offsets` (row r of group g is x[token_of_row[offsets[g]+r]]);

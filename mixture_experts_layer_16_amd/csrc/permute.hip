@@ -174,9 +174,163 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
   }
 }
 
+// ---- reroute policy ("Report sur E2/E3" of the routing slides' overflow
+// table): the q-th dropped slot of a token is offered to its alternate
+// expert alt[t*k+q]; experts accept offers in token order while they have
+// room left after their own first-round rows.
+
+// one thread per token: the candidate expert of each dropped slot (else -1)
+__global__ __launch_bounds__(256) void perm_cand_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ alt,
+    const int32_t* __restrict__ lrank, const int32_t* __restrict__ blk,
+    int32_t* __restrict__ cand, int64_t N, int E, int k, int64_t C) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= N) return;
+  const int64_t b = t / kPermTokens;
+  int q = 0;
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = t * k + j;
+    const int e = idx[a];
+    int c = -1;
+    if (e >= 0 && e < E && C >= 0) {
+      const int64_t r = (int64_t)blk[b * 3 * E + e] + lrank[a];
+      if (r >= C) {
+        c = alt[t * k + q];
+        if (c < 0 || c >= E) c = -1;
+        ++q;
+      }
+    }
+    cand[a] = c;
+  }
+}
+
+// one wave per expert: scan the second-round block histograms into bases,
+// accept min(offers, room), and lay out offsets = first-round rows followed
+// by accepted offers, expert by expert
+__global__ __launch_bounds__(1024) void perm_merge_kernel(
+    int32_t* __restrict__ blk2, int nblk, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ kept1, int E, int64_t C) {
+  __shared__ int32_t k1[kMaxExperts];
+  __shared__ int32_t tot[kMaxExperts];
+  __shared__ int32_t tmp[1024];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) k1[e] = offsets[e + 1] - offsets[e];
+  __syncthreads();
+  for (int e = wave; e < E; e += nwaves) {
+    int carry = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 64) {
+      const int b = b0 + lane;
+      int v = 0;
+      if (b < nblk) v = blk2[(int64_t)b * 3 * E + e];
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      if (b < nblk) blk2[(int64_t)b * 3 * E + e] = carry + incl - v;
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) {
+      const int64_t room = C - k1[e];
+      tot[e] = k1[e] + (int)((int64_t)carry < room ? carry : room);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) kept1[e] = k1[e];
+  const int total = block_exclusive_scan_1024(tot, E, tmp);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = tot[e];
+  if (threadIdx.x == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_reroute_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cand,
+    const int32_t* __restrict__ lrank, const int32_t* __restrict__ blk,
+    const int32_t* __restrict__ lrank2, const int32_t* __restrict__ blk2,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ kept1,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ token_of_row,
+    uint8_t* __restrict__ drop, int32_t* __restrict__ final_idx, int64_t N, int E, int k,
+    int64_t C) {
+  const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (a >= N * k) return;
+  const int64_t t = a / k;
+  const int64_t b = t / kPermTokens;
+  const int e = idx[a];
+  int row = -1, fe = -1;
+  if (e >= 0 && e < E) {
+    const int64_t r = (int64_t)blk[b * 3 * E + e] + lrank[a];
+    if (C < 0 || r < C) {
+      row = offsets[e] + (int)r;
+      fe = e;
+    } else {
+      const int c = cand[a];
+      if (c >= 0) {
+        const int64_t r2 = (int64_t)blk2[b * 3 * E + c] + lrank2[a];
+        if (r2 < C - kept1[c]) {
+          row = offsets[c] + kept1[c] + (int)r2;
+          fe = c;
+        }
+      }
+    }
+  }
+  row_of[a] = row;
+  drop[a] = row < 0 ? 1 : 0;
+  if (row >= 0) token_of_row[row] = (int32_t)t;
+  if (final_idx) final_idx[a] = fe;
+}
+
+__global__ __launch_bounds__(256) void final_idx_kernel(const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ row_of,
+                                                        int32_t* __restrict__ final_idx,
+                                                        int64_t nk) {
+  const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (a < nk) final_idx[a] = row_of[a] >= 0 ? idx[a] : -1;
+}
+
 }  // namespace
 
 int64_t perm_blocks(int64_t N) { return (N + kPermTokens - 1) / kPermTokens; }
+
+hipError_t launch_final_idx(const int32_t* idx, const int32_t* row_of, int32_t* final_idx,
+                            int64_t nk, hipStream_t s) {
+  final_idx_kernel<<<(unsigned)((nk + 255) / 256), 256, 0, s>>>(idx, row_of, final_idx, nk);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_reroute(const int32_t* idx, const int32_t* alt,
+                                  const uint8_t* modality, int32_t* counts,
+                                  int32_t* mod_counts, int32_t* offsets, int32_t* row_of,
+                                  int32_t* token_of_row, uint8_t* drop, int32_t* final_idx,
+                                  int32_t* lrank, int32_t* blk_counts, int32_t* cand,
+                                  int32_t* lrank2, int32_t* blk2, int32_t* kept1, int64_t N,
+                                  int E, int k, int64_t C, hipStream_t s) {
+  const int64_t nblk = perm_blocks(N);
+  const size_t lds = (size_t)(PR_WAVES + 2) * E * sizeof(int32_t);
+  perm_rank_kernel<<<(unsigned)nblk, 256, lds, s>>>(idx, mod_counts ? modality : nullptr,
+                                                     lrank, blk_counts, N, E, k);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  perm_scan_kernel<<<1, 1024, 0, s>>>(blk_counts, (int)nblk, counts, mod_counts, offsets, E, C);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  perm_cand_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(idx, alt, lrank, blk_counts,
+                                                                 cand, N, E, k, C);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  perm_rank_kernel<<<(unsigned)nblk, 256, lds, s>>>(cand, nullptr, lrank2, blk2, N, E, k);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  perm_merge_kernel<<<1, 1024, 0, s>>>(blk2, (int)nblk, offsets, kept1, E, C);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t nk = N * k;
+  perm_scatter_reroute_kernel<<<(unsigned)((nk + 255) / 256), 256, 0, s>>>(
+      idx, cand, lrank, blk_counts, lrank2, blk2, offsets, kept1, row_of, token_of_row, drop,
+      final_idx, N, E, k, C);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const int32_t* idx, const uint8_t* modality, int32_t* counts,
                           int32_t* mod_counts, int32_t* offsets, int32_t* row_of,

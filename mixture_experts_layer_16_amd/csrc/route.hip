@@ -160,7 +160,8 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const double* zpart, int nsplit, const float* __restrict__ logit_bias,
     double* z_out, const float* __restrict__ sel_bias,
     const uint8_t* __restrict__ modality, int n_bias_sets, int gating, int renormalize,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_w, int64_t N, int E, int k) {
+    int32_t* __restrict__ out_idx, float* __restrict__ out_w, int32_t* __restrict__ out_alt,
+    int64_t N, int E, int k) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= N) return;
@@ -191,7 +192,9 @@ __global__ __launch_bounds__(256) void topk_kernel(
 
   int my_e = 0;          // lane r < k: expert of round r
   double my_s = 0.0;     // its logit (softmax) or sigmoid score
-  for (int r = 0; r < k; ++r) {
+  int my_alt = -1;       // lane q < k: expert of round k + q (the alternates)
+  const int ka = out_alt ? min(k, E - k) : 0;
+  for (int r = 0; r < k + ka; ++r) {
     double bk = -INFINITY, bs = 0.0;
     int be = 0x7fffffff;
 #pragma unroll
@@ -211,8 +214,13 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const int owner = be & 63;
     const double ws = __shfl(own_s, owner);
     if (lane == owner) valid &= ~(1u << (be >> 6));
-    if (lane == r) { my_e = be; my_s = ws; }
+    if (r < k) {
+      if (lane == r) { my_e = be; my_s = ws; }
+    } else if (lane == r - k) {
+      my_alt = be;
+    }
   }
+  if (out_alt && lane < k) out_alt[t * k + lane] = my_alt;
 
   // gate weights.  Renormalised: softmax over the chosen logits (equal to the
   // renormalised full softmax), or sigmoid scores divided by their sum.  Raw:
@@ -257,7 +265,34 @@ __global__ __launch_bounds__(256) void topk_kernel(
   }
 }
 
+// Parameter-free router: h = splitmix64(id) (S. Vigna's 64-bit mixer); the
+// token's experts are h mod E, h mod E + 1, ... (mod E), weights 1/k.
+__global__ __launch_bounds__(256) void hash_route_kernel(const int64_t* __restrict__ ids,
+                                                         int64_t N, int E, int k,
+                                                         int32_t* __restrict__ out_idx,
+                                                         float* __restrict__ out_w) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= N) return;
+  uint64_t z = (uint64_t)ids[t] + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  const int base = (int)(z % (uint64_t)E);
+  const float w = 1.0f / (float)k;
+  for (int j = 0; j < k; ++j) {
+    const int e = base + j;
+    out_idx[t * k + j] = e >= E ? e - E : e;
+    out_w[t * k + j] = w;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_hash_route(const int64_t* ids, int64_t N, int E, int k, int32_t* idx,
+                             float* w, hipStream_t s) {
+  hash_route_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(ids, N, E, k, idx, w);
+  return hipGetLastError();
+}
 
 int router_splits(int64_t N, int d, int E) {
   const int64_t base = ((N + RT_TOK - 1) / RT_TOK) * ((E + RT_EXP - 1) / RT_EXP);
@@ -295,13 +330,13 @@ hipError_t launch_router_f32(const float* x, const float* w, double* z, int64_t 
 
 hipError_t launch_topk(const double* zpart, int nsplit, const float* logit_bias, double* z_out,
                        const float* sel_bias, const uint8_t* modality, int n_bias_sets,
-                       int gating, int renormalize, int32_t* idx, float* w, int64_t N, int E,
-                       int k, hipStream_t s) {
+                       int gating, int renormalize, int32_t* idx, float* w, int32_t* alt,
+                       int64_t N, int E, int k, hipStream_t s) {
   const unsigned grid = (unsigned)((N + 3) / 4);
   const int J = (E + 63) / 64;
 #define MOE_TOPK(JJ)                                                                        \
   topk_kernel<JJ><<<grid, 256, 0, s>>>(zpart, nsplit, logit_bias, z_out, sel_bias, modality, \
-                                       n_bias_sets, gating, renormalize, idx, w, N, E, k)
+                                       n_bias_sets, gating, renormalize, idx, w, alt, N, E, k)
   if (J <= 1) MOE_TOPK(1);
   else if (J <= 2) MOE_TOPK(2);
   else if (J <= 4) MOE_TOPK(4);

@@ -392,7 +392,7 @@ def forward(x, k: int, E: int, gating: str, activation: str,
             logit_bias=None, sel_bias=None, modality=None,
             forced_idx: Optional[np.ndarray] = None,
             tokens: Optional[np.ndarray] = None, renormalize: bool = True,
-            forced_w: Optional[np.ndarray] = None) -> dict:
+            forced_w: Optional[np.ndarray] = None, overflow: str = "drop") -> dict:
     """The whole layer: y_t = sum_{j kept} g_tj FFN_{e_tj}(x_t) + sum_s FFN_s(x_t).
 
     [Основы] "Как устроен MoE-слой", step 4; shared expert and drops:
@@ -404,7 +404,8 @@ def forward(x, k: int, E: int, gating: str, activation: str,
     router is not evaluated), otherwise they are recomputed from the scores.
     ``tokens`` restricts the output to those token rows (routing and capacity
     are still decided over the whole batch); the result 'y' then has
-    len(tokens) rows."""
+    len(tokens) rows.  ``overflow="reroute"`` applies dispatch_reroute with the
+    router's alternates instead of dropping."""
     x = np.asarray(x, np.float64)
     N = x.shape[0]
     if forced_w is not None:
@@ -417,13 +418,20 @@ def forward(x, k: int, E: int, gating: str, activation: str,
         idx = r["idx"] if forced_idx is None else np.asarray(forced_idx, np.int64)
         g = gate_weights(r["s"], np.clip(idx, 0, E - 1), renormalize)
     C = capacity(f, N, k, E)
-    disp = dispatch(idx, E, C, modality)
+    if overflow == "reroute":
+        disp = dispatch_reroute(idx, alternates(r["keys"], k), E, C)
+        if modality is not None:
+            disp["modality_counts"] = dispatch(idx, E, C, modality)["modality_counts"]
+        proc = disp["final_idx"]                            # expert processing each slot
+    else:
+        disp = dispatch(idx, E, C, modality)
+        proc = idx
     want = np.arange(N) if tokens is None else np.asarray(tokens, np.int64)
     pos = {int(t): i for i, t in enumerate(want)}
     y = np.zeros((len(want), x.shape[1]), np.float64)
     row_of = disp["row_of"]
     for e in range(E):
-        hit = (idx[want] == e) & (row_of[want] >= 0)        # kept assignments to e
+        hit = (proc[want] == e) & (row_of[want] >= 0)       # kept assignments to e
         rows, slot = np.nonzero(hit)
         if rows.size == 0:
             continue

@@ -59,6 +59,7 @@ class Workload:
     w_std: float = 0.02
     toy_draws: bool = False      # reproduce the NumPy fiche's draw order (toy layer)
     renormalize: bool = True     # gate weights renormalised over the k chosen
+    overflow: str = "drop"       # "drop" | "reroute": fate of assignments past capacity
     notes: str = ""
 
 

@@ -38,7 +38,7 @@ GAMMA = 0.001
 def problem_of(w: synth.Workload, **over):
     kw = dict(S=w.S, gating=w.gating, activation=w.activation, dtype=w.dtype,
               n_bias_sets=w.n_bias_sets, act_clip=w.clip, capacity_factor=w.f,
-              renormalize=int(w.renormalize))
+              renormalize=int(w.renormalize), overflow=w.overflow)
     kw.update(over)
     return L.problem(w.N, w.d, w.E, w.k, w.I, **kw)
 
@@ -57,6 +57,7 @@ def alloc_routing(w, dev="cuda"):
         token_of_row=torch.full((max(1, N * k),), -7, dtype=i32, device=dev),
         drop_mask=torch.full((max(1, N * k),), 7, dtype=torch.uint8, device=dev),
         logits=torch.full((max(1, N * E),), np.nan, dtype=torch.float64, device=dev),
+        final_idx=torch.full((max(1, N * k),), -7, dtype=i32, device=dev),
     )
 
 
@@ -121,7 +122,7 @@ class OracleSide:
                          n_shared=w.S, get_shared=self.shared, w_router=self.wr, clip=w.clip,
                          f=w.f, logit_bias=self.lb, sel_bias=self.sb, modality=self.mod,
                          forced_idx=forced_idx, tokens=tokens, renormalize=w.renormalize,
-                         forced_w=forced_w)
+                         forced_w=forced_w, overflow=w.overflow if forced_w is None else "drop")
 
 
 def check_route(ors: OracleSide, g: dict, report: dict) -> np.ndarray:
@@ -174,6 +175,15 @@ def check_dispatch(ors: OracleSide, g: dict, gidx: np.ndarray, report: dict) -> 
     N, k, E = w.N, w.k, w.E
     C = O.capacity(w.f, N, k, E)
     d = O.dispatch(gidx, E, C, ors.mod if w.n_bias_sets == 2 else None)
+    if w.overflow == "reroute":
+        # the alternates come from the oracle's keys (a near-tie among ranks
+        # k+1 .. 2k would show up as a mismatch here)
+        mc = d["modality_counts"]
+        d = O.dispatch_reroute(gidx, O.alternates(ors.route()["keys"], k), E, C)
+        d["modality_counts"] = mc
+        report["rerouted"] = int(((d["final_idx"] != gidx) & (d["final_idx"] >= 0)).sum())
+    final = d.get("final_idx", np.where(d["row_of"] >= 0, gidx, -1))
+    assert np.array_equal(g["final_idx"][: N * k].reshape(N, k), final)
     assert np.array_equal(g["counts"], d["counts"])
     if w.n_bias_sets == 2:
         assert np.array_equal(g["modality_counts"].reshape(2, E), d["modality_counts"])

@@ -102,17 +102,19 @@ BAD = [  # (overrides, expected status)
     (dict(gating=5), -2), (dict(activation=3), -2), (dict(dtype=4), -2), (dict(n_bias_sets=3), -2),
     (dict(act_clip=float("nan")), -2), (dict(capacity_factor=float("nan")), -2),
     (dict(d=100), -3), (dict(I=36), -3), (dict(renormalize=2), -2), (dict(k=33, E=64), -2),
+    (dict(overflow=2), -2), (dict(overflow=-1), -2),
 ]
 
 
 @pytest.mark.parametrize("over,code", BAD, ids=[str(b[0]) for b in BAD])
 def test_validation_codes(L, over, code):
     base = dict(N=64, d=128, E=8, k=2, I=64, S=1, gating=0, activation=0, dtype=0, n_bias_sets=0,
-                act_clip=0.0, capacity_factor=0.0, renormalize=1)
+                act_clip=0.0, capacity_factor=0.0, renormalize=1, overflow=0)
     base.update(over)
     p = L.Problem(base["N"], base["d"], base["E"], base["k"], base["I"], base["S"],
                   base["gating"], base["activation"], base["dtype"], base["n_bias_sets"],
-                  base["renormalize"], base["act_clip"], base["capacity_factor"])
+                  base["renormalize"], base["act_clip"], base["capacity_factor"],
+                  base["overflow"])
     out = ctypes.c_size_t()
     assert L.LIB.moe_workspace_size(ctypes.byref(p), ctypes.byref(out)) == code
 
@@ -223,3 +225,27 @@ def test_forward_routed_rejects_before_launch(L):
     w2 = L.Weights(None, fake, fake, fake, None, None, None)
     assert lib.moe_forward_routed(B(p), B(w2), fake, fake, fake, None, fake, None, fake,
                                   1 << 30, None) == -1
+
+
+def test_reroute_and_hash_reject_before_launch(L):
+    fake = 0x10000
+    lib = L.LIB
+    B = ctypes.byref
+    pr = L.problem(64, 128, 8, 2, 64, S=1, capacity_factor=1.0, overflow="reroute")
+    # the staged permute and the replay have no alternate experts
+    assert lib.moe_permute(B(pr), fake, None, fake, None, fake, fake, fake, fake, fake, 1 << 20,
+                           None) == -3
+    w = L.Weights(None, fake, fake, fake, fake, fake, fake)
+    assert lib.moe_forward_routed(B(pr), B(w), fake, fake, fake, None, fake, None, fake, 1 << 30,
+                                  None) == -3
+    # hash routing needs ids and outputs
+    p = L.problem(64, 128, 8, 2, 64)
+    assert lib.moe_route_hash(B(p), None, fake, fake, None) == -1
+    assert lib.moe_route_hash(B(p), fake, None, fake, None) == -1
+    assert lib.moe_route_hash(B(L.problem(0, 128, 8, 2, 64)), fake, fake, fake, None) == 0
+
+
+def test_problem_struct_matches_the_header_layout(L):
+    # int64 + 10 int32 + float + double + int32 (padded to 8)
+    assert ctypes.sizeof(L.Problem) == 72
+    assert L.Problem.overflow.offset == 64

@@ -105,3 +105,67 @@ def test_replay_of_arbitrary_routing(name):
         m = float(np.max(err / np.maximum(np.abs(ref["y"]), rms)))
         assert m <= parity.F32_Y_TOL, m
     _say(f"[replay] {name} err {m:.3e} dropped {int(g['drop_mask'][: w.N * w.k].sum())}")
+
+
+REROUTE = {
+    "cap-reroute": dict(base="cap-s", f=1.0),
+    "ds-reroute": dict(base="ds-s", f=1.0),
+    "v41-reroute": dict(base="v41-s", f=1.25),
+    "f32-reroute": dict(base="toy-s", toy_draws=False, f=1.0, zipf_offset=1.0),
+    "k1-reroute": dict(base="cap-s", k=1, f=1.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(REROUTE))
+def test_overflow_reroute(case):
+    """Overflowing slots go to the token's next experts while they have room
+    (routing slides, overflow table, 'Report sur E2/E3')."""
+    import parity
+    spec = dict(REROUTE[case])
+    base = synth.get(spec.pop("base"))
+    w = synth.derive(base, name=f"{base.name}-{case}", overflow="reroute", **spec)
+    _say(f"[reroute] {case} {w}")
+    rep, y, g, _ = parity.full_check(w)
+    _say(f"[reroute] {case} {dict((k, v) for k, v in rep.items() if k != 'modality_counts')}")
+    assert rep["rerouted"] > 0
+
+
+def test_reroute_collapse_fills_other_experts():
+    # every token prefers expert 0: its overflow spreads over the next experts
+    import parity
+    w = synth.derive(synth.get("cap-s"), name="collapse-reroute", N=400, f=1.0,
+                     zipf_offset=0.0, overflow="reroute")
+    inp = synth.make_inputs(w)
+    inp.logit_bias = np.zeros(w.E, np.float32)
+    inp.logit_bias[0] = 50.0
+    rep, y, g, _ = parity.full_check(w, inp=inp)
+    assert rep["rerouted"] > 0
+    C = -(-(w.N * w.k) // w.E)
+    assert np.all(np.diff(g["offsets"]) <= C)
+
+
+def test_hash_router_and_replay():
+    from mixture_experts_layer_16_amd import _lib as L
+    import parity
+    w = synth.get("cap-s")
+    inp = synth.make_inputs(w)
+    di = sdev.upload(inp)
+    rng = np.random.default_rng(11)
+    ids = rng.integers(-(1 << 62), 1 << 62, size=w.N, dtype=np.int64)
+    ids[:3] = [0, 1, -1]
+    p = parity.problem_of(w)
+    idx = torch.full((w.N * w.k,), -7, dtype=torch.int32, device="cuda")
+    gw = torch.full((w.N * w.k,), -7.0, dtype=torch.float32, device="cuda")
+    L.moe_route_hash(p, torch.from_numpy(ids).cuda(), idx, gw)
+    torch.cuda.synchronize()
+    ridx, rg = O.hash_route(ids, w.E, w.k)
+    assert np.array_equal(idx.cpu().numpy().reshape(w.N, w.k), ridx)
+    assert np.all(gw.cpu().numpy() == np.float32(1.0 / w.k))
+    # the layer on the hash routing (capacity applies as usual)
+    y, g = _run_routed(w, di, idx, gw)
+    ors = parity.OracleSide(inp)
+    ref = ors.forward(ridx, forced_w=np.full(ridx.shape, float(np.float32(1.0 / w.k))))
+    d = O.dispatch(ridx, w.E, O.capacity(w.f, w.N, w.k, w.E))
+    assert np.array_equal(g["row_of"][: w.N * w.k].reshape(w.N, w.k), d["row_of"])
+    m = float(np.max(np.abs(parity.y_to_f64(y) - ref["y"]))) / float(np.sqrt(np.mean(ref["y"] ** 2)))
+    assert m <= parity.BF16_Y_TOL, m

@@ -447,6 +447,133 @@ def forward(x, k: int, E: int, gating: str, activation: str,
 
 
 # ---------------------------------------------------------------------------
+# 4b. backward pass (gradients of L = sum(dy * y) for a given upstream dy)
+#
+# The pages give no backward; it is the chain rule through the forward above,
+# with the selection (top-k, capacity, reroute) held fixed -- it is piecewise
+# constant -- so the router is reached only through the gate weights (the
+# reason the Switch top-1 weight is p_i and not 1: [Основы] "Как устроен
+# MoE-слой", variants paragraph).  The clamp passes the gradient where
+# -clip <= silu(a)*u <= clip and stops it outside.  Pinned by central finite
+# differences of the forward.
+
+def expert_ffn_backward(xr, w_gate, w_up, w_down, activation: str, clip: float,
+                        d_out: np.ndarray):
+    """Gradients of out = FFN(xr) for d(out) = d_out: (dx, dW_gate or None,
+    dW_up, dW_down), float64, weights in the library layout."""
+    xr = np.asarray(xr, np.float64)
+    wu = np.asarray(w_up, np.float64)
+    wd = np.asarray(w_down, np.float64)
+    d_out = np.asarray(d_out, np.float64)
+    up = xr @ wu.T
+    if activation == SWIGLU:
+        wg = np.asarray(w_gate, np.float64)
+        a = xr @ wg.T
+        sg = sigmoid(a)
+        act = a * sg
+        hpre = act * up
+        h = np.clip(hpre, -clip, clip) if clip and clip > 0 else hpre
+        dh = d_out @ wd
+        if clip and clip > 0:
+            dh = dh * (np.abs(hpre) <= clip)
+        d_up = dh * act
+        d_a = dh * up * (sg * (1.0 + a * (1.0 - sg)))
+        return d_a @ wg + d_up @ wu, d_a.T @ xr, d_up.T @ xr, d_out.T @ h
+    h = np.maximum(up, 0.0)
+    d_up = (d_out @ wd) * (up > 0)
+    return d_up @ wu, None, d_up.T @ xr, d_out.T @ h
+
+
+def gate_backward(s: np.ndarray, z: np.ndarray, idx: np.ndarray, dg: np.ndarray,
+                  gating: str, renormalize: bool = True) -> np.ndarray:
+    """dz [N, E] from the gate weights' gradient dg [N, k] (gate_weights above,
+    differentiated).  Only the chosen experts (and, for raw softmax weights,
+    every expert through the softmax denominator) receive a gradient."""
+    z = np.asarray(z, np.float64)
+    N, E = z.shape
+    dz = np.zeros((N, E))
+    if N == 0:
+        return dz
+    s = np.asarray(s, np.float64)
+    rows = np.arange(N)[:, None]
+    if gating == SOFTMAX:
+        if renormalize:
+            g = softmax_over_chosen(z, idx)
+            dz[rows, idx] = g * (dg - np.sum(g * dg, axis=1, keepdims=True))
+        else:
+            dp = np.zeros((N, E))
+            dp[rows, idx] = dg
+            dz = s * (dp - np.sum(s * dp, axis=1, keepdims=True))
+    else:
+        sc = np.take_along_axis(s, idx, axis=1)
+        if renormalize:
+            tot = sc.sum(axis=1, keepdims=True)
+            g = sc / tot
+            ds = (dg - np.sum(g * dg, axis=1, keepdims=True)) / tot
+        else:
+            ds = dg
+        dz[rows, idx] = ds * sc * (1.0 - sc)
+    return dz
+
+
+def backward(x, k: int, E: int, gating: str, activation: str,
+             get_expert: Callable[[int], Sequence], n_shared: int = 0,
+             get_shared: Optional[Callable[[int], Sequence]] = None,
+             w_router=None, clip: float = 0.0, f: float = 0.0,
+             logit_bias=None, sel_bias=None, modality=None, dy=None,
+             renormalize: bool = True, overflow: str = "drop") -> dict:
+    """Gradients of L = sum(dy * y) w.r.t. x, every expert's weights, the
+    shared experts, the router and the logit offset, for the routing the
+    forward pass decides.  Returns dx, dW_gate/dW_up/dW_down (lists over
+    experts; None for experts with no kept row), dWs_* (lists over shared
+    experts), dW_router, d_logit_bias, dz, dg."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    N, d = x.shape
+    r = route(x, w_router, k, gating, logit_bias, sel_bias, modality,
+              renormalize=renormalize, check_softmax_identity=False)
+    idx = r["idx"]
+    g = gate_weights(r["s"], idx, renormalize)
+    C = capacity(f, N, k, E)
+    if overflow == "reroute":
+        disp = dispatch_reroute(idx, alternates(r["keys"], k), E, C)
+        proc = disp["final_idx"]
+    else:
+        disp = dispatch(idx, E, C)
+        proc = idx
+    row_of = disp["row_of"]
+    dx = np.zeros_like(x)
+    dg = np.zeros((N, k))
+    dWg, dWu, dWd = [None] * E, [None] * E, [None] * E
+    for e in range(E):
+        hit = (proc == e) & (row_of >= 0)
+        rows, slot = np.nonzero(hit)
+        if rows.size == 0:
+            continue
+        wg, wu, wd = get_expert(e)
+        out = expert_ffn(x[rows], wg, wu, wd, activation, clip)
+        dg[rows, slot] = np.sum(dy[rows] * out, axis=1)
+        d_out = g[rows, slot][:, None] * dy[rows]
+        dxe, dWg[e], dWu[e], dWd[e] = expert_ffn_backward(x[rows], wg, wu, wd, activation,
+                                                          clip, d_out)
+        np.add.at(dx, rows, dxe)
+    dWsg, dWsu, dWsd = [], [], []
+    for s_ in range(n_shared):
+        wg, wu, wd = get_shared(s_)
+        dxs, a_, b_, c_ = expert_ffn_backward(x, wg, wu, wd, activation, clip, dy)
+        dx += dxs
+        dWsg.append(a_)
+        dWsu.append(b_)
+        dWsd.append(c_)
+    dz = gate_backward(r["s"], r["z"], idx, dg, gating, renormalize)
+    dWr = dz.T @ x
+    dx += dz @ np.asarray(w_router, np.float64)
+    return {"dx": dx, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd, "dWs_gate": dWsg,
+            "dWs_up": dWsu, "dWs_down": dWsd, "dW_router": dWr, "d_logit_bias": dz.sum(0),
+            "dz": dz, "dg": dg, "route": r, **disp}
+
+
+# ---------------------------------------------------------------------------
 # 5. load-balancing statistics and the aux-loss-free bias update
 
 def expert_load(counts, N: int, k: int) -> np.ndarray:

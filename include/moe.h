@@ -301,6 +301,57 @@ int moe_balance(const moe_problem* p, const double* logits, const int32_t* count
                 double* aux, float* sel_bias, float gamma, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* Gradients written by moe_backward (device pointers, float32, same layouts
+ * as the weights they belong to). */
+typedef struct {
+  float* dx;            /* [N][d] required */
+  float* dw_router;     /* [E][d] required */
+  float* dw_gate;       /* [E][I][d] required for MOE_SWIGLU, unused for MOE_RELU */
+  float* dw_up;         /* [E][I][d] required */
+  float* dw_down;       /* [E][d][I] required */
+  float* dws_gate;      /* [S][I][d] required when S > 0 and MOE_SWIGLU */
+  float* dws_up;        /* [S][I][d] required when S > 0 */
+  float* dws_down;      /* [S][d][I] required when S > 0 */
+  float* d_logit_bias;  /* [E] nullable: gradient of the logit offset o (= sum_t dz_t) */
+  float* dz;            /* [N][E] nullable: gradient of the logits */
+  float* dg;            /* [N*k] nullable: gradient of the gate weights (0 for dropped slots) */
+} moe_grads;
+
+/* Bytes of device workspace moe_backward needs for problem p (host). */
+int moe_backward_workspace_size(const moe_problem* p, size_t* bytes);
+
+/* Backward pass of the layer: the gradients of L = sum(dy * y) for the routing
+ * a moe_forward call decided, with that routing held fixed (top-k, capacity and
+ * reroute are piecewise constant in the logits, so the router receives its
+ * gradient through the gate weights alone -- why the MoE basics page,
+ * "Основы MoE", section "Как устроен MoE-слой", keeps p_i as the Switch top-1
+ * weight instead of 1).  Chain rule through each step of the forward:
+ *   per kept row (token t, weight g) and shared row (g = 1) of expert FFN f:
+ *     dW_down += (g dy_t)^T h, dh = g dy_t W_down (0 where the clamp is active),
+ *     SwiGLU: da = dh u silu'(a), du = dh silu(a); ReLU: du = dh [u > 0],
+ *     dW_gate += da^T x_t, dW_up += du^T x_t, dx_t += da W_gate + du W_up,
+ *     dg = <dy_t, f(x_t)>;
+ *   gate weights -> logits (softmax renormalised over the chosen, raw softmax
+ *   p, sigmoid renormalised or raw): dz; dW_router = dz^T x, dx += dz W_router,
+ *   d_logit_bias = sum_t dz_t.  Dropped slots get dg = 0 but still move dz
+ *   through the renormalisation.
+ * MOE_BF16 only (MOE_F32 returns MOE_ERR_UNSUPPORTED).  The products run on
+ * the bf16 matrix cores with float32 accumulation: dy and the per-row
+ * gradients (g h, da, du, dz) are rounded to bf16 as operands.
+ *   x        (device) bf16 [N][d], the forward's input
+ *   w        the forward's weights (w_router required)
+ *   routing  (host struct of device pointers) from the moe_forward call:
+ *            topk_idx, topk_w, logits, offsets, row_of, token_of_row required
+ *            (moe_forward writes them when they are given in routing_out)
+ *   dy       (device) float32 [N][d], gradient of the output y
+ *   grads    (host struct of device pointers) outputs, overwritten
+ *   ws       (device) moe_backward_workspace_size() bytes
+ * dy, dx, x and the weights must be 16-byte aligned.  Results are
+ * deterministic (fixed reduction orders, no atomics). */
+int moe_backward(const moe_problem* p, const moe_weights* w, const void* x,
+                 const moe_routing* routing, const float* dy, const moe_grads* grads,
+                 void* ws, size_t ws_bytes, void* stream);
+
 /* Text of a status code (static storage). */
 const char* moe_status_string(int status);
 

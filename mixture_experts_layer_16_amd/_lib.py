@@ -26,8 +26,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_INVALID", -3: "MOE_ERR_U
 # every function include/moe.h declares
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_param_counts", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex",
-           "moe_balance", "moe_forward_routed", "moe_route_hash", "moe_status_string",
-           "moe_version")
+           "moe_balance", "moe_forward_routed", "moe_route_hash", "moe_backward_workspace_size",
+           "moe_backward", "moe_status_string", "moe_version")
 STAGES = ("route", "permute", "plan", "gate_up", "down", "combine")
 
 
@@ -58,6 +58,12 @@ class Routing(ctypes.Structure):
                  "token_of_row", "drop_mask", "logits", "final_idx")]
 
 
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up",
+                 "dws_down", "d_logit_bias", "dz", "dg")]
+
+
 class Profile(ctypes.Structure):
     _fields_ = [("ev", ctypes.c_void_p * (2 * len(STAGES)))]
 
@@ -85,6 +91,9 @@ def _load() -> ctypes.CDLL:
         "moe_forward_routed": [P, ctypes.POINTER(Weights), V, V, V, V, V,
                                ctypes.POINTER(Routing), V, ctypes.c_size_t, V],
         "moe_route_hash": [P, V, V, V, V],
+        "moe_backward_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
+        "moe_backward": [P, ctypes.POINTER(Weights), V, ctypes.POINTER(Routing), V,
+                         ctypes.POINTER(Grads), V, ctypes.c_size_t, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -158,6 +167,13 @@ def moe_param_counts(p: Problem):
     _check("moe_param_counts", LIB.moe_param_counts(ctypes.byref(p), ctypes.byref(a),
                                                     ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def moe_backward_workspace_size(p: Problem) -> int:
+    out = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_size",
+           LIB.moe_backward_workspace_size(ctypes.byref(p), ctypes.byref(out)))
+    return out.value
 
 
 def moe_status_string(status: int) -> str:
@@ -248,6 +264,27 @@ def moe_route_hash(p, token_ids, topk_idx, topk_w, stream=None, raw=False):
     if raw:
         return st
     _check("moe_route_hash", st)
+
+
+def backward_workspace(p: Problem, device="cuda") -> torch.Tensor:
+    """A device byte buffer of moe_backward_workspace_size(p) bytes."""
+    return torch.empty(max(1, moe_backward_workspace_size(p)), dtype=torch.uint8, device=device)
+
+
+def moe_backward(p, w: "Weights", x, routing_in: "Routing", dy, grads_out: "Grads", ws=None,
+                 stream=None, raw=False):
+    st = LIB.moe_backward(ctypes.byref(p), ctypes.byref(w), ptr(x),
+                          ctypes.byref(routing_in) if routing_in is not None else None, ptr(dy),
+                          ctypes.byref(grads_out) if grads_out is not None else None, ptr(ws),
+                          ws.numel() if ws is not None and not isinstance(ws, int) else 0,
+                          _stream(stream))
+    if raw:
+        return st
+    _check("moe_backward", st)
+
+
+def grads(**tensors) -> Grads:
+    return Grads(**{k: ptr(v) for k, v in tensors.items()})
 
 
 def weights(w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None) -> Weights:

@@ -19,7 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "balance.hip"]
+SOURCES = ["abi.hip", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "balance.hip",
+           "backward.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

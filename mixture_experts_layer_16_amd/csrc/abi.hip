@@ -494,6 +494,76 @@ int moe_forward_routed(const moe_problem* p, const moe_weights* w, const void* x
                       ws_bytes, stream, topk_idx, topk_w);
 }
 
+int moe_backward_workspace_size(const moe_problem* p, size_t* bytes) {
+  const int st = validate(p);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = bwd_ws_layout(p).total;
+  return MOE_OK;
+}
+
+int moe_backward(const moe_problem* p, const moe_weights* w, const void* x,
+                 const moe_routing* routing, const float* dy, const moe_grads* grads,
+                 void* ws, size_t ws_bytes, void* stream) {
+  int st = validate(p);
+  if (st) return st;
+  if (!w || !x || !routing || !dy || !grads) return MOE_ERR_NULL;
+  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool swiglu = p->activation == MOE_SWIGLU;
+  const bool shared = p->n_shared > 0;
+  if (!w->w_router || !w->w_up || !w->w_down || (swiglu && !w->w_gate)) return MOE_ERR_NULL;
+  if (shared && (!w->ws_up || !w->ws_down || (swiglu && !w->ws_gate))) return MOE_ERR_NULL;
+  const moe_routing& r = *routing;
+  if (!r.topk_idx || !r.topk_w || !r.logits || !r.offsets || !r.row_of || !r.token_of_row)
+    return MOE_ERR_NULL;
+  const moe_grads& g = *grads;
+  if (!g.dx || !g.dw_router || !g.dw_up || !g.dw_down || (swiglu && !g.dw_gate))
+    return MOE_ERR_NULL;
+  if (shared && (!g.dws_up || !g.dws_down || (swiglu && !g.dws_gate))) return MOE_ERR_NULL;
+  {
+    const void* ptrs[] = {x, w->w_router, w->w_gate, w->w_up, w->w_down, w->ws_gate,
+                          w->ws_up, w->ws_down, dy, g.dx};
+    for (const void* q : ptrs)
+      if (q && !aligned16(q)) return MOE_ERR_UNSUPPORTED;
+  }
+  const BwdLayout L = bwd_ws_layout(p);
+  if (!ws) return MOE_ERR_NULL;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (p->n_tokens == 0) return MOE_OK;
+  BwdCall c{};
+  c.N = p->n_tokens;
+  c.d = p->d_model;
+  c.I = p->d_expert;
+  c.E = p->n_experts;
+  c.k = p->top_k;
+  c.S = p->n_shared;
+  c.gating = p->gating;
+  c.activation = p->activation;
+  c.renormalize = p->renormalize;
+  c.clip = p->act_clip;
+  c.x = x;
+  c.wr = w->w_router;
+  c.wg = w->w_gate; c.wu = w->w_up; c.wd = w->w_down;
+  c.sg = w->ws_gate; c.su = w->ws_up; c.sd = w->ws_down;
+  c.dy = dy;
+  c.logits = r.logits;
+  c.topk_idx = r.topk_idx;
+  c.topk_w = r.topk_w;
+  c.offsets = r.offsets;
+  c.row_of = r.row_of;
+  c.token_of_row = r.token_of_row;
+  c.dx = g.dx;
+  c.dw_router = g.dw_router;
+  c.dw_gate = g.dw_gate; c.dw_up = g.dw_up; c.dw_down = g.dw_down;
+  c.dws_gate = g.dws_gate; c.dws_up = g.dws_up; c.dws_down = g.dws_down;
+  c.d_logit_bias = g.d_logit_bias;
+  c.dz_out = g.dz;
+  c.dg_out = g.dg;
+  c.ws = ws;
+  c.L = L;
+  return launch_backward(c, S(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -1160,4 +1160,12 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   return err;
 }
 
+hipError_t launch_ffn_plan(const int32_t* offsets, int n_gather, int n_ident, int64_t N,
+                           int64_t rows_cap, int64_t ident_row0, int BM, int32_t* plan,
+                           hipStream_t s) {
+  ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, n_gather, n_ident, N, rows_cap, ident_row0, BM,
+                                     BM, plan, nullptr);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -134,6 +134,10 @@ struct FfnCall {
   void* marks[6];              // optional hipEvent_t: before/after plan, gate/up, down
 };
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
+// The tile plan alone (BM-row tiles, no remainder plan), for other grouped GEMMs.
+hipError_t launch_ffn_plan(const int32_t* offsets, int n_gather, int n_ident, int64_t N,
+                           int64_t rows_cap, int64_t ident_row0, int BM, int32_t* plan,
+                           hipStream_t s);
 
 // Balancing statistics: P_e partial sums per block, then load, P, aux and the
 // optional +-gamma update of the selection biases.
@@ -142,6 +146,39 @@ hipError_t launch_balance(const double* z, const int32_t* counts, const int32_t*
                           double* partial, double* load, double* mean_prob, double* aux,
                           float* sel_bias, int n_bias_sets, float gamma, int gating,
                           int64_t N, int E, int k, hipStream_t s);
+
+// Backward pass (bf16 operands, float32 gradients).
+struct BwdLayout {
+  size_t plan, plan_r;     // tile plans: experts + shared; one dense group (router)
+  size_t slot;             // i32 [N*k]  slot of each kept routed row
+  size_t dy16;             // bf16 [N][d]
+  size_t af, uf, dhu;      // f32 [R][I]  a, u recomputed; dy W_down per row
+  size_t hg, da, du;       // bf16 [R][I] g h, da, du
+  size_t dgr;              // f32 [R]     dg of each row
+  size_t dxp;              // f32 [R][d]  per-row input gradient
+  size_t dz;               // f32 [N][E]
+  size_t dz16;             // bf16 [N][Ep]  (E rounded up to 8, zero padded)
+  size_t colsum;           // f64 [blocks][E]
+  size_t total;
+};
+BwdLayout bwd_ws_layout(const moe_problem* p);
+struct BwdCall {
+  int64_t N;
+  int d, I, E, k, S;
+  int gating, activation, renormalize;
+  float clip;
+  const void* x;                               // bf16 [N][d]
+  const void *wr, *wg, *wu, *wd, *sg, *su, *sd;
+  const float* dy;                             // f32 [N][d]
+  const double* logits;                        // [N][E]
+  const int32_t *topk_idx, *offsets, *row_of, *token_of_row;
+  const float* topk_w;
+  float *dx, *dw_router, *dw_gate, *dw_up, *dw_down, *dws_gate, *dws_up, *dws_down;
+  float *d_logit_bias, *dz_out, *dg_out;       // nullable
+  void* ws;
+  BwdLayout L;
+};
+hipError_t launch_backward(const BwdCall& c, hipStream_t s);
 
 hipError_t launch_combine(int dtype, const void* y_rows, const int32_t* row_of,
                           const float* topk_w, const void* y_shared, int64_t shared_stride_rows,

@@ -34,6 +34,7 @@ import numpy as np
 # tensor ids used in SeedSequence([seed, tensor_id, expert])
 T_X, T_ROUTER, T_WGATE, T_WUP, T_WDOWN, T_SGATE, T_SUP, T_SDOWN = range(8)
 T_SELBIAS, T_MODALITY, T_X_DECODE, T_X_IMAGE, T_X_IMAGE_DECODE = 8, 9, 10, 11, 12
+T_DY = 13
 
 
 @dataclass(frozen=True)
@@ -202,6 +203,11 @@ def logit_offset(w: Workload) -> Optional[np.ndarray]:
         return None
     e = np.arange(1, w.E + 1, dtype=np.float64)
     return (e ** (-w.zipf_offset)).astype(np.float32)
+
+
+def upstream_grad(w: Workload) -> np.ndarray:
+    """float32 [N][d] ~ N(0, 1): the gradient dL/dy fed to the backward pass."""
+    return _normal(_rng(w.seed, T_DY), (w.N, w.d), 0.0, 1.0)
 
 
 def selection_bias(w: Workload) -> Optional[np.ndarray]:

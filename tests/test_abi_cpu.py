@@ -249,3 +249,60 @@ def test_problem_struct_matches_the_header_layout(L):
     # int64 + 10 int32 + float + double + int32 (padded to 8)
     assert ctypes.sizeof(L.Problem) == 72
     assert L.Problem.overflow.offset == 64
+
+
+def test_backward_rejects_before_launch(L):
+    fake = 0x10000
+    lib = L.LIB
+    B = ctypes.byref
+    p = L.problem(64, 128, 8, 2, 64, S=1)
+    w = L.Weights(fake, fake, fake, fake, fake, fake, fake)
+    r = L.Routing(topk_idx=fake, topk_w=fake, logits=fake, offsets=fake, row_of=fake,
+                  token_of_row=fake)
+    g = L.Grads(dx=fake, dw_router=fake, dw_gate=fake, dw_up=fake, dw_down=fake, dws_gate=fake,
+                dws_up=fake, dws_down=fake)
+    big = 1 << 40
+
+    def call(p_=p, w_=w, x=fake, r_=r, dy=fake, g_=g, ws=fake, nb=big):
+        return lib.moe_backward(B(p_), B(w_), x, B(r_) if r_ is not None else None, dy,
+                                B(g_) if g_ is not None else None, ws, nb, None)
+
+    # missing arguments, routing arrays, gradients or weights
+    assert call(x=None) == -1 and call(dy=None) == -1
+    assert call(r_=None) == -1 and call(g_=None) == -1
+    for f in ("topk_idx", "topk_w", "logits", "offsets", "row_of", "token_of_row"):
+        r2 = L.Routing(**{n: getattr(r, n) for n, _ in L.Routing._fields_})
+        setattr(r2, f, None)
+        assert call(r_=r2) == -1, f
+    for f in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down"):
+        g2 = L.Grads(**{n: getattr(g, n) for n, _ in L.Grads._fields_})
+        setattr(g2, f, None)
+        assert call(g_=g2) == -1, f
+    assert call(w_=L.Weights(None, fake, fake, fake, fake, fake, fake)) == -1
+    # ReLU experts need no gate matrices or their gradients
+    pr = L.problem(64, 128, 8, 2, 64, S=1, activation="relu")
+    wr = L.Weights(fake, None, fake, fake, None, fake, fake)
+    gr = L.Grads(dx=fake, dw_router=fake, dw_up=fake, dw_down=fake, dws_up=fake, dws_down=fake)
+    assert call(p_=pr, w_=wr, g_=gr, nb=16) == -4
+    # float32 operands are not supported; misaligned dy; small workspace
+    assert call(p_=L.problem(64, 128, 8, 2, 64, S=1, dtype="f32")) == -3
+    assert call(dy=fake + 4) == -3
+    assert call(nb=16) == -4
+    assert call(ws=None) == -1
+    # an empty batch is a no-op
+    need = L.moe_backward_workspace_size(L.problem(0, 128, 8, 2, 64, S=1))
+    assert call(p_=L.problem(0, 128, 8, 2, 64, S=1), nb=need) == 0
+
+
+def test_backward_workspace_grows_with_tokens(L):
+    a = L.moe_backward_workspace_size(L.problem(100, 128, 8, 2, 64, S=1))
+    b = L.moe_backward_workspace_size(L.problem(200, 128, 8, 2, 64, S=1))
+    c = L.moe_backward_workspace_size(L.problem(200, 128, 8, 2, 64, S=1, activation="relu"))
+    assert 0 < a < b and c < b
+    # the per-row float32 buffers dominate: (k + S) rows per token of I and d floats
+    assert b - a >= 100 * 3 * (3 * 64 * 4 + 128 * 4)
+
+
+def test_grads_struct_matches_the_header_layout(L):
+    assert ctypes.sizeof(L.Grads) == 11 * 8
+    assert L.Grads.dg.offset == 80

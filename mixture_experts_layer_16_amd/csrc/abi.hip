@@ -521,8 +521,10 @@ int moe_backward(const moe_problem* p, const moe_weights* w, const void* x,
     return MOE_ERR_NULL;
   if (shared && (!g.dws_up || !g.dws_down || (swiglu && !g.dws_gate))) return MOE_ERR_NULL;
   {
-    const void* ptrs[] = {x, w->w_router, w->w_gate, w->w_up, w->w_down, w->ws_gate,
-                          w->ws_up, w->ws_down, dy, g.dx};
+    const void* ptrs[] = {x,          w->w_router, w->w_gate,  w->w_up,   w->w_down,
+                          w->ws_gate, w->ws_up,    w->ws_down, dy,        g.dx,
+                          g.dw_router, g.dw_gate,  g.dw_up,    g.dw_down, g.dws_gate,
+                          g.dws_up,   g.dws_down};
     for (const void* q : ptrs)
       if (q && !aligned16(q)) return MOE_ERR_UNSUPPORTED;
   }

@@ -25,33 +25,24 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-constexpr int GB_M = 128, GB_N = 128, GB_K = 32;   // tile and k-slice
-constexpr int GB_STAGE = (GB_M + GB_N) * GB_K;     // elements per LDS stage
+constexpr int BW_BN = 256;   // tile columns
 
-// LDS row layout: rows of 32 k-values (64 bytes), two per 128-byte line; the
-// 16-byte chunk at position q of line l sits at q ^ swz(l) (conflict-free for
-// the 32-row fragment reads, as in the forward kernels)
-__device__ __forceinline__ int bw_swz(int line) { return ((line >> 1) & 3) ^ ((line & 1) << 1); }
-__device__ __forceinline__ int bw_off(int row, int chunk) {   // element offset of (row, chunk*8)
-  const int line = row >> 1;
-  return line * 64 + ((((row & 1) << 2) + chunk) ^ bw_swz(line)) * 8;
-}
-
-// One operand of C[m][n] = sum_k A(m,k) B(n,k).
-//   T == 0: element (i, k) at p[row(i) * ld + k]            (k contiguous)
-//   T == 1: element (i, k) at p[row(k) * ld + i]            (i contiguous)
-// row() applies the optional row map (a gather), else the identity plus a
-// base row.  Rows past the tile's extent are clamped; k past the slice's K
-// reads zero.
+// One operand of C[m][n] = sum_k A(m, k) B(n, k).
+//   T == 0: element (i, k) at row(i)[k]   (k contiguous; i = m or n)
+//   T == 1: element (i, k) at row(k)[i]   (i contiguous)
+// row(r) = base + r' * ld, with base = p + g * gstride for routed groups and
+// ps + (g - n_gather) * gstride for dense ones; r' = r, except for a dense
+// group of an operand whose rows are tokens (dense_tok): r' = r - the group's
+// first layout row.  Rows past an extent are clamped; k past K reads zero.
 struct Operand {
-  const uint16_t* p;    // routed groups (group g at p + g * gstride), or the only matrix
-  const uint16_t* ps;   // dense (shared-expert) groups: group g at ps + (g - n_gather) * gstride
-  int64_t gstride;      // 0: the same matrix for every group
+  const uint16_t* p;
+  const uint16_t* ps;
+  int64_t gstride;
   int64_t ld;
-  int tokens;           // rows are layout rows to turn into token rows: through map for
-                        // routed groups, minus the dense group's first row otherwise
-  const int32_t* map;   // token_of_row
+  int dense_tok;
 };
 
 struct BwdGemmParams {
@@ -60,7 +51,7 @@ struct BwdGemmParams {
   float* C;                  // row mode: [rows][ldc]; weight mode: routed groups' matrices
   float* Cs;                 // weight mode: dense groups' matrices
   int64_t ldc, c_gstride;
-  int M, N, K, K2;           // fixed extents (row mode: M from the plan; weight mode: K)
+  int M, N, K, K2;           // extents (row mode: M from the plan; weight mode: K from it)
   int mode;                  // 0: tiles over the plan's rows; 1: K = a group's rows
   const int32_t* plan;       // tile_start[G+1], row_begin[G], rows[G]
   int G;
@@ -68,21 +59,79 @@ struct BwdGemmParams {
   int64_t ident_row0, n_tokens;
 };
 
-template <int TA, int TB>
-__global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdGemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sm[2 * GB_STAGE];
+// ---------------------------------------------------------------------------
+// Grouped GEMM with direct-to-LDS copies, either operand transposed.
+//
+// A block computes a BM x 256 tile of C with 8 waves (4 x 2, each (BM/4) x 128
+// of v_mfma_f32_32x32x16_bf16 accumulators), k-slices of 64 in two LDS stages.
+// Copies go from global memory straight into LDS (global_load_lds_dwordx4: one
+// wave instruction fills 1 KiB = 8 lines of 128 bytes; each lane picks the
+// 16-byte global chunk that belongs at its own position), so both layouts
+// below are produced without passing through registers:
+//   T == 0: one line per row (64 k), chunk c (k 8c .. 8c+7) at position
+//           c ^ sw0(line);
+//   T == 1: one k-row of the slice takes R/64 lines (R = 256 or BM rows of the
+//           operand); quarter q (i 64q .. 64q+63) is line (R/64) k + (q ^ (k & 1))
+//           and chunk c of it (i 64q + 8c ..) sits at position c ^ sw1(k).
+// T == 0 fragments are one ds_read_b128 per lane.  T == 1 fragments are read
+// transposed with ds_read_b64_tr_b16: in each 16-lane group, lane j names the
+// 4 consecutive elements of k-row k0 + j/4 at i0 + 4 (j%4), and lane j
+// receives element j%4 of lanes 4q + j/4, q = 0..3, i.e. k0 .. k0+3 of i0 + j
+// -- two such reads give a lane its 8 consecutive k of one row of the
+// fragment, the matrix-core operand layout.  Both swizzles keep the reads of
+// a half wave on distinct banks.
+//
+// The schedule follows the forward kernels: each 16-wide step issues its
+// MFMAs with the next step's fragment reads (and, in the last step of a
+// slice, the copies of a later slice) between them; one barrier per slice;
+// NS stages in a ring.  Results are float32: the B fragment is the first MFMA
+// operand, so the accumulators hold C^T with runs of 4 consecutive columns per
+// lane, which go through LDS to leave as whole 128-byte row segments.
+__device__ __forceinline__ int sw0(int line) { return (line & 7) ^ ((line >> 3) & 1); }
+__device__ __forceinline__ int sw1(int k) { return 2 * (k & 3); }
+
+__device__ __forceinline__ void bw_g2lds16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ const uint32_t kBwZero[4] = {0u, 0u, 0u, 0u};
+
+template <int TA, int TB, int BM, int BK, int NW, int NS>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) {
+  constexpr int BN = BW_BN, KS = BK / 16;
+  constexpr int LA = BM * BK / 64, LB = BN * BK / 64;   // 128-byte lines per operand and stage
+  constexpr int SB = (LA + LB) * 128;          // bytes per stage
+  constexpr int NLD = (LA + LB) / (8 * NW);    // copies per thread per slice
+  constexpr int JA = LA / (8 * NW);            // the first JA copies are A's
+  constexpr int WM = NW / 2;
+  constexpr int WROWS = BM / WM, WCOLS = BN / 2;
+  constexpr int FM = WROWS / 32, FN = WCOLS / 32;
+  constexpr int NRA = FM * (TA ? 2 : 1), NRB = FN * (TB ? 2 : 1);   // read instructions
+  static_assert(BM == 128 || BM == 256, "tile rows");
+  static_assert(NW == 4 || NW == 8, "waves");
+  static_assert(BK == 64 || (BK == 32 && TA == 1 && TB == 1), "k-slice (32: transposed operands)");
+  static_assert(JA * 8 * NW == LA && NLD * 8 * NW == LA + LB, "copies cover the stage");
+  static_assert(NS >= 2 && (NS - 1) * NLD <= 63 && KS % 2 == 0, "pipeline shape");
+  static_assert(NS * SB <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[NS * SB];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- tile decode
   int g, m0, n0, Mlim, Klim;
   int64_t rb;
-  const int ntn = (p.N + GB_N - 1) / GB_N;
+  const int ntn = (p.N + BN - 1) / BN;
   if (p.mode == 0) {
     const int32_t* tile_start = p.plan;
     const int total = tile_start[p.G] * ntn;
-    const int L = blockIdx.x;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    if (slot >= per) return;
+    const int L = (blockIdx.x % kXcds) * per + slot;   // consecutive tiles on one XCD
     if (L >= total) return;
     int lo = 0, hi = p.G - 1;
     while (lo < hi) {
@@ -90,204 +139,314 @@ __global__ __launch_bounds__(256, 2) void bwd_gemm_kernel(BwdGemmParams p) {
       if (tile_start[mid] * ntn <= L) lo = mid; else hi = mid - 1;
     }
     g = lo;
+    // within a group: super-rows of GM m-tiles, m-tile fastest inside one, so
+    // the tiles running together on one XCD share weight rows (the large
+    // operand) and a few row tiles
+    constexpr int GM = 8;
+    const int mtg = tile_start[g + 1] - tile_start[g];
     const int local = L - tile_start[g] * ntn;
-    m0 = (local / ntn) * GB_M;
-    n0 = (local % ntn) * GB_N;
+    const int sr = local / (GM * ntn);
+    const int rem = local - sr * GM * ntn;
+    const int gm = min(GM, mtg - sr * GM);
+    const int nt = rem / gm;
+    m0 = (sr * GM + (rem - nt * gm)) * BM;
+    n0 = nt * BN;
     rb = p.plan[p.G + 1 + g];
     Mlim = p.plan[p.G + 1 + p.G + g];
     Klim = p.K;
   } else {
-    const int ntm = (p.M + GB_M - 1) / GB_M;
+    const int ntm = (p.M + BM - 1) / BM;
     const int per = ntm * ntn;
-    g = blockIdx.x / per;
-    if (g >= p.G) return;
-    const int local = blockIdx.x - g * per;
-    m0 = (local / ntn) * GB_M;
-    n0 = (local % ntn) * GB_N;
+    const int total = per * p.G;
+    const int pxcd = (total + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    if (slot >= pxcd) return;
+    const int L = (blockIdx.x % kXcds) * pxcd + slot;
+    if (L >= total) return;
+    g = L / per;
+    const int local = L - g * per;
+    // the smaller operand's tiles vary fastest, so it stays in L2 while the
+    // larger one streams through once
+    if (p.M <= p.N) {
+      m0 = (local % ntm) * BM;
+      n0 = (local / ntm) * BN;
+    } else {
+      m0 = (local / ntn) * BM;
+      n0 = (local % ntn) * BN;
+    }
     rb = p.plan[p.G + 1 + g];
     Klim = p.plan[p.G + 1 + p.G + g];
+    Mlim = p.M;
     if (Klim <= 0) {
       // no rows: the gradient of this group's weights is zero
       float* Cg = g < p.n_gather ? p.C + g * p.c_gstride
                                  : p.Cs + (int64_t)(g - p.n_gather) * p.c_gstride;
-      for (int i = tid; i < GB_M * GB_N; i += 256) {
-        const int m = m0 + i / GB_N, n = n0 + i % GB_N;
-        if (m < p.M && n < p.N) Cg[(int64_t)m * p.ldc + n] = 0.f;
+      for (int i = tid; i < BM * BN / 4; i += 64 * NW) {
+        const int m = m0 + i / (BN / 4), n = n0 + 4 * (i % (BN / 4));
+        if (m < p.M && n < p.N)
+          *reinterpret_cast<float4*>(Cg + (int64_t)m * p.ldc + n) = make_float4(0.f, 0.f, 0.f, 0.f);
       }
       return;
     }
-    Mlim = p.M;
   }
+  const bool routed = g < p.n_gather;
+  const int64_t dense_row0 = p.ident_row0 + (int64_t)(g - p.n_gather) * p.n_tokens;
+  auto row_ptr = [&](const Operand& O, int64_t r) -> const char* {
+    if (O.dense_tok && !routed) r -= dense_row0;
+    const uint16_t* base =
+        routed ? O.p + g * O.gstride : O.ps + (int64_t)(g - p.n_gather) * O.gstride;
+    return reinterpret_cast<const char*>(base + r * O.ld);
+  };
 
-  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t lds_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * 1024;
+  const int lline = lane >> 3, lpos = lane & 7;
+
+  // fragment read offsets (bytes within a stage) for step kk = 0; a step adds
+  // 32 bytes (T == 0) or 16 k-rows (T == 1)
+  const int wm = wave % WM, wn = wave / WM;
   const int lr = lane & 31, lh = lane >> 5;
-  f32x16_t acc[2][2];
+  const int tg = lane >> 4, tj = lane & 15;
+  auto tr_off = [&](int region, int lpk, int o, int h) {
+    // element (k, o) with k = 8 (tg >> 1) + 4 h + tj / 4 and o + 16 (tg & 1) + 4 (tj & 3)
+    const int k = 8 * (tg >> 1) + 4 * h + (tj >> 2);
+    const int i = o + 16 * (tg & 1) + 4 * (tj & 3);
+    const int q = i >> 6, c = (i >> 3) & 7, b = i & 7;
+    return region + (lpk * k + (q ^ (k & 1))) * 128 + ((c ^ sw1(k)) << 4) + b * 2;
+  };
+
+  f32x16_t acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // group-dependent operand bases: routed weight groups move by the group
-  // stride; in row mode, operands indexed by rows use the plan's row begin
-  const bool routed = g < p.n_gather;
-  const int64_t dense_row0 = p.ident_row0 + (int64_t)(g - p.n_gather) * p.n_tokens;
   auto run = [&](const Operand& OA, const Operand& OB, int K) {
-    // per-thread load plans
-    //  T == 0: thread -> rows (tid/4) + 64*i, chunk tid%4: two 16-byte loads
-    //  T == 1: thread -> k pair 2*(tid/16), rows 8*(tid%16) .. +7: two loads
-    auto row_ptr = [&](const Operand& O, int64_t rr) -> const uint16_t* {
-      if (O.tokens) {
-        if (routed) {
-          rr = O.map[rr];
-          rr = rr < 0 ? 0 : (rr >= p.n_tokens ? p.n_tokens - 1 : rr);
-        } else {
-          rr -= dense_row0;
-        }
-      }
-      const uint16_t* base =
-          routed ? O.p + g * O.gstride : O.ps + (int64_t)(g - p.n_gather) * O.gstride;
-      return base + rr * O.ld;
-    };
-    // extents: A's rows are m (limit Mlim), B's rows are n (limit N); in
-    // weight mode the k rows are the group's rows (limit Klim)
-    u32x4_t ra[2], rbv[2];
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    auto load = [&](int k0) {
+    // ---- copy sources.  Copy j of this wave fills stage line (NW j + wave) 8
+    // + lane / 8 at position lane % 8.
+    const char* src[NLD];
+    int kof[NLD];            // k of the chunk (T == 0) or of the k-row (T == 1)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (TA == 0) {
-          int m = m0 + (tid >> 2) + 64 * i;
-          if (m >= Mlim) m = Mlim - 1;
-          const int kk = k0 + (tid & 3) * 8;
-          const uint16_t* q = row_ptr(OA, p.mode == 0 ? rb + m : (int64_t)m);
-          ra[i] = kk < K ? *reinterpret_cast<const u32x4_t*>(q + kk) : zero;
-        } else {
-          // 8 consecutive rows; the operand's rows are padded to a multiple of 8
-          const int kk = k0 + 2 * (tid >> 4) + i;
-          int m = m0 + 8 * (tid & 15);
-          if (m >= Mlim) m = ((Mlim + 7) & ~7) - 8;
-          if (kk < K) {
-            const uint16_t* q = row_ptr(OA, p.mode == 1 ? rb + kk : (int64_t)kk);
-            ra[i] = *reinterpret_cast<const u32x4_t*>(q + m);
-          } else {
-            ra[i] = zero;
-          }
-        }
-        if (TB == 0) {
-          int n = n0 + (tid >> 2) + 64 * i;
-          if (n >= p.N) n = p.N - 1;
-          const int kk = k0 + (tid & 3) * 8;
-          const uint16_t* q = row_ptr(OB, n);
-          rbv[i] = kk < K ? *reinterpret_cast<const u32x4_t*>(q + kk) : zero;
-        } else {
-          const int kk = k0 + 2 * (tid >> 4) + i;
-          int n = n0 + 8 * (tid & 15);
-          if (n >= p.N) n = ((p.N + 7) & ~7) - 8;
-          if (kk < K) {
-            const uint16_t* q = row_ptr(OB, p.mode == 1 ? rb + kk : (int64_t)kk);
-            rbv[i] = *reinterpret_cast<const u32x4_t*>(q + n);
-          } else {
-            rbv[i] = zero;
-          }
-        }
-      }
-    };
-    auto store = [&](uint16_t* s) {
-      uint16_t* sa = s;
-      uint16_t* sb = s + GB_M * GB_K;
-      if (TA == 0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          *reinterpret_cast<u32x4_t*>(sa + bw_off((tid >> 2) + 64 * i, tid & 3)) = ra[i];
+    for (int j = 0; j < NLD; ++j) {
+      const bool isA = j < JA;
+      const int T = isA ? TA : TB;
+      const int line = (NW * j + wave) * 8 + lline - (isA ? 0 : LA);
+      const int rows = isA ? BM : BN;
+      const Operand& O = isA ? OA : OB;
+      const int lim = isA ? Mlim : p.N;
+      const int i0 = isA ? m0 : n0;
+      if (T == 0) {
+        const int c = lpos ^ sw0(line);
+        int i = i0 + line;
+        if (i >= lim) i = lim - 1;
+        const int64_t r = (isA && p.mode == 0) ? rb + i : (int64_t)i;
+        src[j] = row_ptr(O, r) + c * 16;
+        kof[j] = 8 * c;
       } else {
-        // rows 8*(tid%16)+c get the k pair 2*(tid/16), 2*(tid/16)+1
-        const int kp = 2 * (tid >> 4);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t lo = (ra[0][c >> 1] >> (16 * (c & 1))) & 0xffffu;
-          const uint32_t hi = (ra[1][c >> 1] >> (16 * (c & 1))) & 0xffffu;
-          const int row = 8 * (tid & 15) + c;
-          *reinterpret_cast<uint32_t*>(sa + bw_off(row, kp >> 3) + (kp & 7)) = lo | (hi << 16);
-        }
+        const int lpk = rows / 64;
+        const int k = line / lpk;
+        const int q = (line % lpk) ^ (k & 1);
+        const int c = lpos ^ sw1(k);
+        int i = i0 + 64 * q + 8 * c;
+        if (i >= lim) i = ((lim + 7) & ~7) - 8;
+        const int64_t r = (p.mode == 1 ? rb : 0) + k;
+        src[j] = row_ptr(O, r) + (int64_t)i * 2;
+        kof[j] = k;
       }
-      if (TB == 0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          *reinterpret_cast<u32x4_t*>(sb + bw_off((tid >> 2) + 64 * i, tid & 3)) = rbv[i];
-      } else {
-        const int kp = 2 * (tid >> 4);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t lo = (rbv[0][c >> 1] >> (16 * (c & 1))) & 0xffffu;
-          const uint32_t hi = (rbv[1][c >> 1] >> (16 * (c & 1))) & 0xffffu;
-          const int row = 8 * (tid & 15) + c;
-          *reinterpret_cast<uint32_t*>(sb + bw_off(row, kp >> 3) + (kp & 7)) = lo | (hi << 16);
-        }
-      }
-    };
-    auto compute = [&](const uint16_t* s) {
-      const uint16_t* sa = s;
-      const uint16_t* sb = s + GB_M * GB_K;
-#pragma unroll
-      for (int kk = 0; kk < GB_K / 16; ++kk) {
-        u32x4_t af[2], bf[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = *reinterpret_cast<const u32x4_t*>(sa + bw_off(wm * 64 + 32 * i + lr, 2 * kk + lh));
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bf[j] = *reinterpret_cast<const u32x4_t*>(sb + bw_off(wn * 64 + 32 * j + lr, 2 * kk + lh));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, bf[j]),
-                acc[i][j], 0, 0, 0);
-      }
-    };
-    const int nsl = (K + GB_K - 1) / GB_K;
-    if (nsl <= 0) return;
-    load(0);
-    store(sm);
-    __syncthreads();
-    for (int kt = 0; kt < nsl; ++kt) {
-      uint16_t* cur = sm + (kt & 1) * GB_STAGE;
-      uint16_t* nxt = sm + ((kt + 1) & 1) * GB_STAGE;
-      if (kt + 1 < nsl) load((kt + 1) * GB_K);
-      compute(cur);
-      if (kt + 1 < nsl) store(nxt);
-      __syncthreads();
     }
+    const int64_t stepA = TA ? (int64_t)BK * OA.ld * 2 : BK * 2;   // bytes per slice
+    const int64_t stepB = TB ? (int64_t)BK * OB.ld * 2 : BK * 2;
+    const int nsl = (K + BK - 1) / BK;
+    auto src_of = [&](int j, int kt) -> const char* {
+      const bool ok = kt * BK + kof[j] < K;   // false for slices past the last
+      return ok ? src[j] + kt * (j < JA ? stepA : stepB) : reinterpret_cast<const char*>(kBwZero);
+    };
+    auto issue_slice = [&](int st, int kt) {
+      const uint32_t sb = lds_base + st * SB;
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) bw_g2lds16(src_of(j, kt), sb + NW * 1024 * j);
+    };
+
+    int aoff[NRA], boff[NRB];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int o = wm * WROWS + 32 * i;
+      if (TA == 0) {
+        aoff[i] = (o + lr) * 128 + (((lh) ^ sw0(o + lr)) << 4);
+      } else {
+        aoff[2 * i] = tr_off(0, BM / 64, o, 0);
+        aoff[2 * i + 1] = tr_off(0, BM / 64, o, 1);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int o = wn * WCOLS + 32 * j;
+      if (TB == 0) {
+        boff[j] = LA * 128 + (o + lr) * 128 + (((lh) ^ sw0(o + lr)) << 4);
+      } else {
+        boff[2 * j] = tr_off(LA * 128, BN / 64, o, 0);
+        boff[2 * j + 1] = tr_off(LA * 128, BN / 64, o, 1);
+      }
+    }
+    // step kk: T == 0 chunk 2 kk + lh (the swizzle is an XOR on the chunk:
+    // (2kk + lh) ^ s = ((lh ^ s) ^ 2kk), so the offset moves by XOR 32 kk bytes);
+    // T == 1: 16 k-rows further
+    auto rd_a = [&](int i, int kk, const char* s) -> u32x4_t {
+      if (TA == 0) {
+        const int off = aoff[i] ^ (32 * kk);
+        return *reinterpret_cast<const u32x4_t*>(s + off);
+      } else {
+        const int adv = 16 * (BM / 64) * 128 * kk;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((__attribute__((address_space(3))) char*)(s) + aoff[2 * i] + adv));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((__attribute__((address_space(3))) char*)(s) + aoff[2 * i + 1] + adv));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        return u32x4_t{l2.x, l2.y, h2.x, h2.y};
+      }
+    };
+    auto rd_b = [&](int j, int kk, const char* s) -> u32x4_t {
+      if (TB == 0) {
+        const int off = boff[j] ^ (32 * kk);
+        return *reinterpret_cast<const u32x4_t*>(s + off);
+      } else {
+        const int adv = 16 * (BN / 64) * 128 * kk;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((__attribute__((address_space(3))) char*)(s) + boff[2 * j] + adv));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((__attribute__((address_space(3))) char*)(s) + boff[2 * j + 1] + adv));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        return u32x4_t{l2.x, l2.y, h2.x, h2.y};
+      }
+    };
+    auto read_frags = [&](int st, int kk, u32x4_t (&af)[FM], u32x4_t (&bf)[FN]) {
+      const char* s = lds + st * SB;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = rd_a(i, kk, s);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bf[j] = rd_b(j, kk, s);
+    };
+    // one 16-wide step: MFMA m, then the next step's fragment m (when RD) and
+    // this MFMA's share of the copies of slice dkt into stage dst (when DMA)
+    auto step = [&](auto RD, auto DMA, const u32x4_t (&af)[FM], const u32x4_t (&bf)[FN],
+                    int rst, int rkk, u32x4_t (&na)[FM], u32x4_t (&nb)[FN], int dst, int dkt) {
+      constexpr bool kRd = decltype(RD)::value;
+      constexpr bool kDma = decltype(DMA)::value;
+      constexpr int NM = FM * FN, NF = FM + FN;
+      const char* rs = lds + rst * SB;
+      const uint32_t sb = lds_base + dst * SB;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int i = m / FN, j = m % FN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, bf[j]), __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j],
+            0, 0, 0);
+        if constexpr (kRd) {
+          // the NF fragments spread over the NM MFMAs
+#pragma unroll
+          for (int r = m * NF / NM; r < (m + 1) * NF / NM; ++r) {
+            if (r < FM) na[r] = rd_a(r, rkk, rs);
+            else nb[r - FM] = rd_b(r - FM, rkk, rs);
+          }
+        }
+        if constexpr (kDma) {
+#pragma unroll
+          for (int d = m * NLD / NM; d < (m + 1) * NLD / NM; ++d)
+            bw_g2lds16(src_of(d, dkt), sb + NW * 1024 * d);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+
+    if (nsl <= 0) return;
+    // NS-stage ring: slice kt lives in stage kt % NS.  Prologue: slices 0 ..
+    // NS-1.  At the end of slice kt: wait for slice kt+1 (slices kt+2 ..
+    // kt+NS-1 may still be in flight), the barrier that publishes it and frees
+    // stage kt % NS, then the last 16-wide step of slice kt with the copies of
+    // slice kt+NS into that stage and the first fragment reads of slice kt+1
+    // in its shadow.  Slices past the last copy the zero chunk into stages no
+    // slice reads, so every wait counts the same number of copies.
+    u32x4_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    int st = 0;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) issue_slice(q, q);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * NLD) : "memory");
+    __syncthreads();
+    read_frags(0, 0, fa0, fb0);
+    for (int kt = 0; kt + 1 < nsl; ++kt) {
+      const int nx = (st + 1 == NS) ? 0 : st + 1;
+#pragma unroll
+      for (int kk = 0; kk + 1 < KS; ++kk) {
+        if (kk % 2 == 0) step(T_{}, F_{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+        else step(T_{}, F_{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+      }
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD) : "memory");
+      __syncthreads();
+      step(T_{}, T_{}, fa1, fb1, nx, 0, fa0, fb0, st, kt + NS);
+      st = nx;
+    }
+#pragma unroll
+    for (int kk = 0; kk + 1 < KS; ++kk) {
+      if (kk % 2 == 0) step(T_{}, F_{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+      else step(T_{}, F_{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+    }
+    step(F_{}, F_{}, fa1, fb1, 0, 0, fa0, fb0, 0, 0);
+    // every copy has landed and every wave is done with the stages before
+    // they are refilled (second product) or the block ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   };
   run(p.A, p.B, p.mode == 1 ? Klim : p.K);
   if (p.two) run(p.A2, p.B2, p.mode == 1 ? Klim : p.K2);
 
-  // ---- store: element v of lane: row 8*(v/4) + 4*lh + v%4, column lr
+  // ---- store: acc[i][j] is the 32 x 32 block of C^T; element v of lane
+  // (lr, lh) is row 32 i + lr and column 8 (v / 4) + 4 lh + v % 4 of fragment j,
+  // so each lane holds runs of 4 consecutive columns
   float* C = p.C;
   if (p.mode == 1)
     C = routed ? p.C + g * p.c_gstride : p.Cs + (int64_t)(g - p.n_gather) * p.c_gstride;
+  {
+    // through LDS (free: run() ended with a barrier after its last reads), one
+    // 32-column fragment per pass, so each global store instruction writes
+    // whole 128-byte row segments (measured: 8% less time for the backward on
+    // the 256-expert layer than 32-byte pieces straight from the accumulators)
+    constexpr int PS = 32 * 4 + 16;   // LDS row stride in bytes (padded)
+    static_assert(NW * WROWS * PS <= NS * SB, "epilogue staging fits the stages");
+    char* eb = lds + wave * (WROWS * PS);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < FN; ++j) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * lh + (v & 3);
-      if (m >= Mlim) continue;
-      const int64_t crow = (p.mode == 0 ? rb + m : (int64_t)m) * p.ldc;
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + 32 * j + lr;
-        if (n < p.N) C[crow + n] = acc[i][j][v];
+        for (int vq = 0; vq < 4; ++vq)
+          *reinterpret_cast<float4*>(eb + (32 * i + lr) * PS + (8 * vq + 4 * lh) * 4) =
+              make_float4(acc[i][j][4 * vq], acc[i][j][4 * vq + 1], acc[i][j][4 * vq + 2],
+                          acc[i][j][4 * vq + 3]);
+      // the LDS operations of one wave complete in order: the reads see the
+      // writes, and the next pass's writes come after these reads
+#pragma unroll
+      for (int q = 0; q < WROWS / 8; ++q) {
+        const int row = 8 * q + (lane >> 3), c4 = lane & 7;
+        const float4 v = *reinterpret_cast<const float4*>(eb + row * PS + c4 * 16);
+        const int m = m0 + wm * WROWS + row;
+        const int n = n0 + wn * WCOLS + 32 * j + 4 * c4;
+        if (m < Mlim && n < p.N)
+          *reinterpret_cast<float4*>(C + (p.mode == 0 ? rb + m : (int64_t)m) * p.ldc + n) = v;
       }
     }
+  }
 }
 
-template <int TA, int TB>
-hipError_t launch_bwd_gemm(const BwdGemmParams& p, int64_t blocks, hipStream_t s) {
-  if (blocks <= 0) return hipSuccess;
-  bwd_gemm_kernel<TA, TB><<<(unsigned)blocks, 256, 0, s>>>(p);
+template <int TA, int TB, int BM, int BK = 64, int NW = 8, int NS = 2>
+hipError_t launch_bwd_gemm(const BwdGemmParams& p, int64_t tiles, hipStream_t s) {
+  if (tiles <= 0) return hipSuccess;
+  // the decode deals tiles to the XCDs in blocks of ceil(tiles / 8)
+  const int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
+  bwd_gemm_dl<TA, TB, BM, BK, NW, NS><<<(unsigned)blocks, 64 * NW, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -320,6 +479,29 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ 
   o.x = f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
   o.y = f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
   reinterpret_cast<uint2*>(b)[i] = o;
+}
+
+// Routed rows of x and dy in the forward's row layout: xg[r] = x[t], dyg[r] =
+// bf16(dy[t]) for t = token_of_row[r], r < offsets[E]; 8 columns per thread.
+__global__ __launch_bounds__(256) void gather_rows_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ dy,
+    const int32_t* __restrict__ token_of_row, const int32_t* __restrict__ offsets, int E,
+    int64_t N, int d, uint16_t* __restrict__ xg, uint16_t* __restrict__ dyg) {
+  const int64_t r = blockIdx.x;
+  if (r >= offsets[E]) return;
+  int64_t t = token_of_row[r];
+  t = t < 0 ? 0 : (t >= N ? N - 1 : t);
+  for (int c = 8 * threadIdx.x; c < d; c += 8 * 256) {
+    *reinterpret_cast<u32x4_t*>(xg + r * d + c) = *reinterpret_cast<const u32x4_t*>(x + t * d + c);
+    const float4 a = *reinterpret_cast<const float4*>(dy + t * d + c);
+    const float4 b = *reinterpret_cast<const float4*>(dy + t * d + c + 4);
+    u32x4_t o;
+    o[0] = f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+    o[1] = f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+    o[2] = f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
+    o[3] = f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
+    *reinterpret_cast<u32x4_t*>(dyg + r * d + c) = o;
+  }
 }
 
 // slot (t*k + j) of each kept routed row
@@ -551,6 +733,8 @@ BwdLayout bwd_ws_layout(const moe_problem* p) {
   L.plan_r = take(plan_bytes(1));
   L.slot = take(nk * 4);
   L.dy16 = take(N * d * 2);
+  L.xg = take(nk * d * 2);
+  L.dyg = take(nk * d * 2);
   L.af = swiglu ? take(R * I * 4) : 0;
   L.uf = take(R * I * 4);
   L.dhu = take(R * I * 4);
@@ -579,6 +763,8 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   int32_t* plan_r = reinterpret_cast<int32_t*>(base + L.plan_r);
   int32_t* slot = reinterpret_cast<int32_t*>(base + L.slot);
   uint16_t* dy16 = reinterpret_cast<uint16_t*>(base + L.dy16);
+  uint16_t* xg = reinterpret_cast<uint16_t*>(base + L.xg);
+  uint16_t* dyg = reinterpret_cast<uint16_t*>(base + L.dyg);
   float* af = swiglu ? reinterpret_cast<float*>(base + L.af) : nullptr;
   float* uf = reinterpret_cast<float*>(base + L.uf);
   float* dhu = reinterpret_cast<float*>(base + L.dhu);
@@ -599,11 +785,20 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
     if (err != hipSuccess) return err; \
   } while (0)
 
+  // Row tiles of BM = 256 rows when the groups are large, else 128 (a group
+  // of r rows costs ceil(r / BM) tiles).
+  const int bm = (R / G >= 512) ? 256 : 128;
+  const int bmr = N >= 512 ? 256 : 128;
   // tile plans: experts + shared experts over the forward's row layout, and
   // one dense group of N rows for the router products
-  MOE_CHK(launch_ffn_plan(c.offsets, E, S, N, nk, nk, GB_M, plan, s));
-  MOE_CHK(launch_ffn_plan(nullptr, 0, 1, N, 0, 0, GB_M, plan_r, s));
-  to_bf16_kernel<<<blocks_of(N * d / 4, 256), 256, 0, s>>>(c.dy, dy16, N * d / 4);
+  MOE_CHK(launch_ffn_plan(c.offsets, E, S, N, nk, nk, bm, plan, s));
+  MOE_CHK(launch_ffn_plan(nullptr, 0, 1, N, 0, 0, bmr, plan_r, s));
+  if (S > 0) {
+    to_bf16_kernel<<<blocks_of(N * d / 4, 256), 256, 0, s>>>(c.dy, dy16, N * d / 4);
+    MOE_CHK(hipGetLastError());
+  }
+  gather_rows_kernel<<<(unsigned)nk, 256, 0, s>>>(x, c.dy, c.token_of_row, c.offsets, E, N, d,
+                                                  xg, dyg);
   MOE_CHK(hipGetLastError());
   slot_of_row_kernel<<<blocks_of(nk, 256), 256, 0, s>>>(c.row_of, slot, nk);
   MOE_CHK(hipGetLastError());
@@ -615,10 +810,26 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   q.ident_row0 = nk;
   q.n_tokens = N;
   // tiles of the row-mode products: at most one partial tile per group
-  const int64_t row_tiles = (nk + GB_M - 1) / GB_M + E + S * ((N + GB_M - 1) / GB_M);
-  auto tn = [](int n) { return (int64_t)((n + GB_N - 1) / GB_N); };
-  const Operand xin{x, x, 0, d, 1, c.token_of_row};
-  const Operand dyin{dy16, dy16, 0, d, 1, c.token_of_row};
+  const int64_t row_tiles = (nk + bm - 1) / bm + E + S * ((N + bm - 1) / bm);
+  auto tn = [](int n) { return (int64_t)((n + BW_BN - 1) / BW_BN); };
+#ifndef MOE_BWD_RNS
+#define MOE_BWD_RNS 2, 3
+#endif
+  auto row_gemm = [&](auto TBc, const BwdGemmParams& pp, int64_t tiles) {
+    constexpr int TB_ = decltype(TBc)::value;
+    constexpr int ns[2] = {MOE_BWD_RNS};   // stages for 256- and 128-row tiles
+    return bm == 256 ? launch_bwd_gemm<0, TB_, 256, 64, 8, ns[0]>(pp, tiles, s)
+                     : launch_bwd_gemm<0, TB_, 128, 64, 8, ns[1]>(pp, tiles, s);
+  };
+  using TN = std::integral_constant<int, 0>;
+  using TT = std::integral_constant<int, 1>;
+  // routed rows come from the gathered copies, dense (shared-expert) rows from
+  // the token arrays
+  const Operand xin{xg, x, 0, d, 1};
+  const Operand dyin{dyg, dy16, 0, d, 1};
+  auto Wop = [&](const void* r_, const void* s_, int64_t ld) {
+    return Operand{W(r_), W(s_), (int64_t)I * d, ld, 0};
+  };
 
   // recompute a = x W_gate^T and u = x W_up^T per row
   q.mode = 0;
@@ -627,18 +838,18 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   q.ldc = I;
   q.A = xin;
   if (swiglu) {
-    q.B = Operand{W(c.wg), W(c.sg), (int64_t)I * d, d, 0, nullptr};
+    q.B = Wop(c.wg, c.sg, d);
     q.C = af;
-    MOE_CHK((launch_bwd_gemm<0, 0>(q, row_tiles * tn(I), s)));
+    MOE_CHK(row_gemm(TN{}, q, row_tiles * tn(I)));
   }
-  q.B = Operand{W(c.wu), W(c.su), (int64_t)I * d, d, 0, nullptr};
+  q.B = Wop(c.wu, c.su, d);
   q.C = uf;
-  MOE_CHK((launch_bwd_gemm<0, 0>(q, row_tiles * tn(I), s)));
-  // du_h = dy W_down (W_down [d][I] read with the reduction index slow)
+  MOE_CHK(row_gemm(TN{}, q, row_tiles * tn(I)));
+  // du_h = dy W_down (W_down [d][I]: the reduction index is its row)
   q.A = dyin;
-  q.B = Operand{W(c.wd), W(c.sd), (int64_t)d * I, I, 0, nullptr};
+  q.B = Wop(c.wd, c.sd, I);
   q.C = dhu;
-  MOE_CHK((launch_bwd_gemm<0, 1>(q, row_tiles * tn(I), s)));
+  MOE_CHK(row_gemm(TT{}, q, row_tiles * tn(I)));
 
   bwd_rows_kernel<<<(unsigned)R, 256, 0, s>>>(af, uf, dhu, slot, c.topk_w, c.offsets, E, nk, I,
                                               swiglu ? 1 : 0, c.clip, hg, da, du, dgr);
@@ -646,25 +857,30 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
 
   // weight gradients, one group per expert: K = the group's rows
   q.mode = 1;
-  const Operand hgin{hg, hg, 0, I, 0, nullptr};
-  const Operand dain{da, da, 0, I, 0, nullptr};
-  const Operand duin{du, du, 0, I, 0, nullptr};
-  auto wblocks = [&](int M, int Nn) {
-    return (int64_t)G * ((M + GB_M - 1) / GB_M) * tn(Nn);
+  const Operand hgin{hg, hg, 0, I, 0};
+  const Operand dain{da, da, 0, I, 0};
+  const Operand duin{du, du, 0, I, 0};
+#ifndef MOE_BWD_WCFG
+#define MOE_BWD_WCFG 256, 32, 8, 3
+#endif
+  auto wgemm = [&](const BwdGemmParams& pp, int M, int Nn) {
+    constexpr int cfg[4] = {MOE_BWD_WCFG};   // tile rows, k-slice, waves, stages
+    const int64_t tiles = (int64_t)G * ((M + cfg[0] - 1) / cfg[0]) * tn(Nn);
+    return launch_bwd_gemm<1, 1, cfg[0], cfg[1], cfg[2], cfg[3]>(pp, tiles, s);
   };
-  // dW_down[e] = sum_r (g dy_t)^T h_r   ([d][I])
+  // dW_down[e] = sum_r dy_t^T (g h_r)   ([d][I])
   q.M = d; q.N = I; q.ldc = I; q.c_gstride = (int64_t)d * I;
   q.A = dyin; q.B = hgin; q.C = c.dw_down; q.Cs = c.dws_down;
-  MOE_CHK((launch_bwd_gemm<1, 1>(q, wblocks(d, I), s)));
+  MOE_CHK(wgemm(q, d, I));
   // dW_gate[e] = sum_r da_r^T x_t, dW_up[e] = sum_r du_r^T x_t   ([I][d])
   q.M = I; q.N = d; q.ldc = d; q.c_gstride = (int64_t)I * d;
   q.B = xin;
   if (swiglu) {
     q.A = dain; q.C = c.dw_gate; q.Cs = c.dws_gate;
-    MOE_CHK((launch_bwd_gemm<1, 1>(q, wblocks(I, d), s)));
+    MOE_CHK(wgemm(q, I, d));
   }
   q.A = duin; q.C = c.dw_up; q.Cs = c.dws_up;
-  MOE_CHK((launch_bwd_gemm<1, 1>(q, wblocks(I, d), s)));
+  MOE_CHK(wgemm(q, I, d));
 
   // per-row input gradient dx_r = da W_gate + du W_up ([R][d])
   q.mode = 0;
@@ -672,16 +888,16 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   q.C = dxp; q.Cs = nullptr;
   if (swiglu) {
     q.A = dain;
-    q.B = Operand{W(c.wg), W(c.sg), (int64_t)I * d, d, 0, nullptr};
+    q.B = Wop(c.wg, c.sg, d);
     q.A2 = duin;
-    q.B2 = Operand{W(c.wu), W(c.su), (int64_t)I * d, d, 0, nullptr};
+    q.B2 = Wop(c.wu, c.su, d);
     q.two = 1;
   } else {
     q.A = duin;
-    q.B = Operand{W(c.wu), W(c.su), (int64_t)I * d, d, 0, nullptr};
+    q.B = Wop(c.wu, c.su, d);
     q.two = 0;
   }
-  MOE_CHK((launch_bwd_gemm<0, 1>(q, row_tiles * tn(d), s)));
+  MOE_CHK(row_gemm(TT{}, q, row_tiles * tn(d)));
   q.two = 0;
 
   // router: dz from the gate weights' gradient
@@ -699,20 +915,22 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   qr.K = E;
   qr.N = d;
   qr.ldc = d;
-  qr.A = Operand{dz16, dz16, 0, Ep, 0, nullptr};
-  qr.B = Operand{W(c.wr), W(c.wr), 0, d, 0, nullptr};
+  qr.A = Operand{dz16, dz16, 0, Ep, 0};
+  qr.B = Operand{W(c.wr), W(c.wr), 0, d, 0};
   qr.C = c.dx;
-  MOE_CHK((launch_bwd_gemm<0, 1>(qr, ((N + GB_M - 1) / GB_M) * tn(d), s)));
+  const int64_t rtiles = ((N + bmr - 1) / bmr) * tn(d);
+  MOE_CHK(bmr == 256 ? (launch_bwd_gemm<0, 1, 256>(qr, rtiles, s))
+                     : (launch_bwd_gemm<0, 1, 128>(qr, rtiles, s)));
   // dW_router = dz^T x ([E][d])
   qr.mode = 1;
   qr.M = E;
   qr.N = d;
   qr.ldc = d;
   qr.c_gstride = 0;
-  qr.B = Operand{x, x, 0, d, 0, nullptr};
+  qr.B = Operand{x, x, 0, d, 0};
   qr.C = c.dw_router;
   qr.Cs = c.dw_router;
-  MOE_CHK((launch_bwd_gemm<1, 1>(qr, (int64_t)((E + GB_M - 1) / GB_M) * tn(d), s)));
+  MOE_CHK((launch_bwd_gemm<1, 1, 256>(qr, (int64_t)((E + 255) / 256) * tn(d), s)));
   if (c.d_logit_bias) {
     const int64_t nb = colsum_blocks(N);
     const int64_t chunk = (N + nb - 1) / nb;

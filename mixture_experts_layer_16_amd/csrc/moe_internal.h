@@ -152,6 +152,7 @@ struct BwdLayout {
   size_t plan, plan_r;     // tile plans: experts + shared; one dense group (router)
   size_t slot;             // i32 [N*k]  slot of each kept routed row
   size_t dy16;             // bf16 [N][d]
+  size_t xg, dyg;          // bf16 [N*k][d]  x and dy of each routed row
   size_t af, uf, dhu;      // f32 [R][I]  a, u recomputed; dy W_down per row
   size_t hg, da, du;       // bf16 [R][I] g h, da, du
   size_t dgr;              // f32 [R]     dg of each row

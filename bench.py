@@ -114,6 +114,62 @@ def cpu_baseline(w, inp, budget_s=15.0):
             "host_cpu_count": len(os.sched_getaffinity(0))}
 
 
+def cpu_baseline_backward(w, inp, budget_s=15.0):
+    """Time the float64 oracle's backward (as it is) on a bounded sample: the
+    batch of the first n tokens (same weights and layer), n sized to the
+    budget.  Returns the dict for the JSON line."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        blas = ",".join(sorted({f"{i.get('internal_api')}" for i in info}))
+    except Exception:  # pragma: no cover
+        threads, blas = len(os.sched_getaffinity(0)), "unknown"
+    x = synth.to_f64(w, inp.x)
+    wr = synth.to_f64(w, inp.w_router)
+    dy = synth.upstream_grad(w).astype(np.float64)
+    lb = None if inp.logit_bias is None else inp.logit_bias.astype(np.float64)
+    sb = None if inp.sel_bias is None else inp.sel_bias.astype(np.float64)
+    cache = {}
+
+    def get(e, shared=False):
+        key = (shared, e)
+        if key not in cache:
+            arrs = inp.shared(e) if shared else inp.expert(e)
+            cache[key] = tuple(None if a is None else synth.to_f64(w, a) for a in arrs)
+        return cache[key]
+
+    for e in range(w.E):
+        get(e)
+    for s in range(w.S):
+        get(s, True)
+
+    def run(n):
+        mod = None if inp.modality is None else inp.modality[:n]
+        t = time.perf_counter()
+        O.backward(x[:n], w.k, w.E, w.gating, w.activation, get_expert=get, n_shared=w.S,
+                   get_shared=lambda s: get(s, True), w_router=wr, clip=w.clip, f=w.f,
+                   logit_bias=lb, sel_bias=sb, modality=mod, dy=dy[:n],
+                   renormalize=w.renormalize, overflow=w.overflow)
+        return time.perf_counter() - t
+
+    n2 = min(w.N, 64)
+    t = run(n2)
+    # grow the sample until it takes about the budget (the first runs include
+    # one-time costs, so one extrapolation step can fall short)
+    while n2 < w.N and t < 0.5 * budget_s:
+        n2 = int(min(w.N, max(2 * n2, n2 * budget_s / max(t, 1e-6))))
+        t = run(n2)
+    return {"value": n2 / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 NumPy oracle ({blas} BLAS): backward of the batch of the first "
+                       f"{n2} tokens ({t:.2f} s; same weights, layer options and capacity "
+                       f"factor); value = {n2} / time"),
+            "host_cpu_count": len(os.sched_getaffinity(0))}
+
+
 def pmc_traffic(kernel: str, workload: str, src_hash: str):
     """HBM traffic of one launch from a committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
@@ -137,6 +193,9 @@ def main():
     ap.add_argument("--workload", default="cap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (moe_backward on the forward's routing) "
+                         "instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the run, copy 256 MiB device-to-device once: a kernel of known "
                          "traffic to scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
@@ -166,6 +225,8 @@ def main():
     p = L.problem(w.N, w.d, w.E, w.k, w.I, S=w.S, gating=w.gating, activation=w.activation,
                   dtype=w.dtype, n_bias_sets=w.n_bias_sets, act_clip=w.clip,
                   capacity_factor=w.f)
+    if args.backward:
+        return bench_backward(args, w, inp, di, p)
     ws = L.workspace(p)
     y = torch.empty((w.N, w.d), dtype=torch.float32, device="cuda")
     offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
@@ -283,6 +344,144 @@ def main():
         "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / PEAK_MFMA_TFLOPS,
                   "gbs": layer_gbs, "hbm_frac": layer_gbs / PEAK_HBM_GBS,
                   "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                  "ms_per_step_events": ms_step_ev},
+        "stages_ms": acc,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_backward(args, w, inp, di, p):
+    """The backward pass: forward once for the routing, then K timed calls of
+    moe_backward (all gradients: x, every expert, shared experts, router,
+    logit offset).  Dominant stage: the three weight-gradient grouped GEMMs."""
+    import numpy as np
+    import torch
+    import synth
+    from mixture_experts_layer_16_amd import _lib as L
+
+    dev = "cuda"
+    N, d, E, k, I, S = w.N, w.d, w.E, w.k, w.I, w.S
+    i32, f32 = torch.int32, torch.float32
+    rt_t = dict(topk_idx=torch.empty(N * k, dtype=i32, device=dev),
+                topk_w=torch.empty(N * k, dtype=f32, device=dev),
+                offsets=torch.empty(E + 1, dtype=i32, device=dev),
+                row_of=torch.empty(N * k, dtype=i32, device=dev),
+                token_of_row=torch.empty(N * k, dtype=i32, device=dev),
+                logits=torch.empty(N * E, dtype=torch.float64, device=dev))
+    wts = L.weights(di.w_router, di.w_gate, di.w_up, di.w_down, di.ws_gate, di.ws_up, di.ws_down)
+    rt = L.routing(**rt_t)
+    ws = L.workspace(p)
+    y = torch.empty((N, d), dtype=f32, device=dev)
+    L.moe_forward(p, wts, di.x, di.logit_bias, di.sel_bias, di.modality, y, rt, ws)
+    torch.cuda.synchronize()
+    del ws, y
+    swiglu = w.activation == "swiglu"
+    g = dict(dx=torch.empty((N, d), dtype=f32, device=dev),
+             dw_router=torch.empty((E, d), dtype=f32, device=dev),
+             dw_up=torch.empty((E, I, d), dtype=f32, device=dev),
+             dw_down=torch.empty((E, d, I), dtype=f32, device=dev),
+             d_logit_bias=torch.empty(E, dtype=f32, device=dev))
+    if swiglu:
+        g["dw_gate"] = torch.empty((E, I, d), dtype=f32, device=dev)
+    if S:
+        g["dws_up"] = torch.empty((S, I, d), dtype=f32, device=dev)
+        g["dws_down"] = torch.empty((S, d, I), dtype=f32, device=dev)
+        if swiglu:
+            g["dws_gate"] = torch.empty((S, I, d), dtype=f32, device=dev)
+    dy = torch.from_numpy(synth.upstream_grad(w)).to(dev)
+    bws = L.backward_workspace(p)
+    gr = L.grads(**g)
+    stream = torch.cuda.current_stream()
+    log(f"backward: workspace {bws.numel() / 2**30:.2f} GiB, gradients "
+        f"{sum(t.numel() for t in g.values()) * 4 / 2**30:.2f} GiB")
+
+    def step(prof=None):
+        L.moe_backward_ex(p, wts, di.x, rt, dy, gr, prof, bws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    profs = [L.profile({("wgrad", 0): a, ("wgrad", 1): b}, L.BSTAGES) for a, b in evs]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(profs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    ms_step_ev = e0.elapsed_time(e1) / K
+    wg_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    log(f"timed {K} backward steps: {ms_step:.4f} ms/step wall, {ms_step_ev:.4f} ms/step "
+        f"events, weight gradients {wg_ms:.4f} ms")
+    stage_ev = {(s_, j): torch.cuda.Event(enable_timing=True) for s_ in L.BSTAGES for j in (0, 1)}
+    for ev in stage_ev.values():
+        ev.record(stream)
+    torch.cuda.synchronize()
+    sprof = L.profile(stage_ev, L.BSTAGES)
+    acc = {s_: 0.0 for s_ in L.BSTAGES}
+    reps = 5
+    for _ in range(reps):
+        step(sprof)
+        torch.cuda.synchronize()
+        for s_ in L.BSTAGES:
+            acc[s_] += stage_ev[(s_, 0)].elapsed_time(stage_ev[(s_, 1)]) / reps
+    log("backward stages ms: " + ", ".join(f"{s_}={v:.4f}" for s_, v in acc.items()))
+
+    off = rt_t["offsets"].cpu().numpy()
+    A = int(off[-1])
+    rows = A + N * S
+    m = 3 if swiglu else 2
+    # chain-rule flops: dh 2dI, weight gradients 2dI each, dx 2dI per matrix
+    # with a reduction over I (gate, up); router dW and dx 2NdE each.  The
+    # recomputation of a and u (m-1 products) is counted apart.
+    flops = (1 + m + (m - 1)) * 2 * d * I * rows + 4 * N * d * E
+    flops_recompute = (m - 1) * 2 * d * I * rows
+    wg_flops = m * 2 * d * I * rows          # the weight-gradient stage: m launches
+    per_launch = wg_flops / m
+    ach = per_launch / (wg_ms / m * 1e-3) / 1e12
+    src = open(os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc", "backward.hip"),
+               "rb").read()
+    kname = "bwd_gemm_wgrad"
+    roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_MFMA_TFLOPS,
+            "traffic": pmc_traffic(kname, w.name, hashlib.sha256(src).hexdigest()),
+            "kernel": kname, "launches_per_step": m, "ms_per_launch": wg_ms / m,
+            "algorithmic_per_launch": per_launch}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 CPU oracle's backward on a bounded sample ...")
+        cpu = cpu_baseline_backward(w, inp, args.cpu_budget)
+        log(f"cpu oracle backward {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+    out = {
+        "metric": "MoE-layer backward tokens/s at 1 GPU",
+        "value": N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init weights of the stated shapes; dy ~ N(0, 1))",
+        "config": {"workload": w.name, "pass": "backward", "N": N, "d": d, "E": E, "S": S,
+                   "k": k, "I": I, "capacity_factor": w.f, "gating": w.gating,
+                   "activation": w.activation, "kept_assignments": A},
+        "layer": {"tflops": flops / (ms_step * 1e-3) / 1e12,
+                  "mfma_frac": flops / (ms_step * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS,
+                  "algorithmic_flops": flops, "recompute_flops": flops_recompute,
                   "ms_per_step_events": ms_step_ev},
         "stages_ms": acc,
         "roofline": roof,

@@ -352,6 +352,24 @@ int moe_backward(const moe_problem* p, const moe_weights* w, const void* x,
                  const moe_routing* routing, const float* dy, const moe_grads* grads,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* Stages of moe_backward, in launch order (indices into moe_profile.ev, as
+ * for the forward's stages). */
+enum {
+  MOE_BSTAGE_PREP = 0,       /* tile plans, routed rows of x and dy gathered */
+  MOE_BSTAGE_RECOMPUTE = 1,  /* a = x W_gate^T, u = x W_up^T per row */
+  MOE_BSTAGE_DH = 2,         /* dy W_down per row */
+  MOE_BSTAGE_ROWS = 3,       /* per-row activation gradients and dg */
+  MOE_BSTAGE_WGRAD = 4,      /* dW_down, dW_gate, dW_up grouped GEMMs */
+  MOE_BSTAGE_DX = 5,         /* per-row dx, router gradients, dx combine */
+  MOE_NUM_BSTAGES = 6
+};
+
+/* moe_backward with an optional measurement hook (prof may be NULL; then it is
+ * exactly moe_backward).  ev[2*i] and ev[2*i+1] bracket backward stage i. */
+int moe_backward_ex(const moe_problem* p, const moe_weights* w, const void* x,
+                    const moe_routing* routing, const float* dy, const moe_grads* grads,
+                    const moe_profile* prof, void* ws, size_t ws_bytes, void* stream);
+
 /* Text of a status code (static storage). */
 const char* moe_status_string(int status);
 

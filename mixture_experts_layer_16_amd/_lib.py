@@ -27,8 +27,9 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_INVALID", -3: "MOE_ERR_U
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_param_counts", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex",
            "moe_balance", "moe_forward_routed", "moe_route_hash", "moe_backward_workspace_size",
-           "moe_backward", "moe_status_string", "moe_version")
+           "moe_backward", "moe_backward_ex", "moe_status_string", "moe_version")
 STAGES = ("route", "permute", "plan", "gate_up", "down", "combine")
+BSTAGES = ("prep", "recompute", "dh", "rows", "wgrad", "dx")
 
 
 class MoeError(RuntimeError):
@@ -94,6 +95,9 @@ def _load() -> ctypes.CDLL:
         "moe_backward_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
         "moe_backward": [P, ctypes.POINTER(Weights), V, ctypes.POINTER(Routing), V,
                          ctypes.POINTER(Grads), V, ctypes.c_size_t, V],
+        "moe_backward_ex": [P, ctypes.POINTER(Weights), V, ctypes.POINTER(Routing), V,
+                            ctypes.POINTER(Grads), ctypes.POINTER(Profile), V, ctypes.c_size_t,
+                            V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -283,6 +287,19 @@ def moe_backward(p, w: "Weights", x, routing_in: "Routing", dy, grads_out: "Grad
     _check("moe_backward", st)
 
 
+def moe_backward_ex(p, w: "Weights", x, routing_in: "Routing", dy, grads_out: "Grads",
+                    prof=None, ws=None, stream=None, raw=False):
+    st = LIB.moe_backward_ex(ctypes.byref(p), ctypes.byref(w), ptr(x),
+                             ctypes.byref(routing_in) if routing_in is not None else None,
+                             ptr(dy), ctypes.byref(grads_out) if grads_out is not None else None,
+                             ctypes.byref(prof) if prof is not None else None, ptr(ws),
+                             ws.numel() if ws is not None and not isinstance(ws, int) else 0,
+                             _stream(stream))
+    if raw:
+        return st
+    _check("moe_backward_ex", st)
+
+
 def grads(**tensors) -> Grads:
     return Grads(**{k: ptr(v) for k, v in tensors.items()})
 
@@ -313,10 +330,11 @@ def moe_forward(p, w: Weights, x, logit_bias, sel_bias, modality, y, routing_out
     _check("moe_forward", st)
 
 
-def profile(events: dict) -> Profile:
+def profile(events: dict, stages=STAGES) -> Profile:
     """Profile struct from {(stage_name, 0|1): torch.cuda.Event} (0 = before,
-    1 = after).  Each event must already exist (record it once first)."""
+    1 = after); stages = STAGES (forward) or BSTAGES (backward).  Each event
+    must already exist (record it once first)."""
     pr = Profile()
     for (name, which), ev in events.items():
-        pr.ev[2 * STAGES.index(name) + which] = ev.cuda_event
+        pr.ev[2 * stages.index(name) + which] = ev.cuda_event
     return pr

@@ -505,6 +505,12 @@ int moe_backward_workspace_size(const moe_problem* p, size_t* bytes) {
 int moe_backward(const moe_problem* p, const moe_weights* w, const void* x,
                  const moe_routing* routing, const float* dy, const moe_grads* grads,
                  void* ws, size_t ws_bytes, void* stream) {
+  return moe_backward_ex(p, w, x, routing, dy, grads, nullptr, ws, ws_bytes, stream);
+}
+
+int moe_backward_ex(const moe_problem* p, const moe_weights* w, const void* x,
+                    const moe_routing* routing, const float* dy, const moe_grads* grads,
+                    const moe_profile* prof, void* ws, size_t ws_bytes, void* stream) {
   int st = validate(p);
   if (st) return st;
   if (!w || !x || !routing || !dy || !grads) return MOE_ERR_NULL;
@@ -563,6 +569,8 @@ int moe_backward(const moe_problem* p, const moe_weights* w, const void* x,
   c.dg_out = g.dg;
   c.ws = ws;
   c.L = L;
+  if (prof)
+    for (int i = 0; i < 2 * MOE_NUM_BSTAGES; ++i) c.marks[i] = prof->ev[i];
   return launch_backward(c, S(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

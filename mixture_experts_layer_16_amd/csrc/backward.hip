@@ -57,6 +57,12 @@ struct BwdGemmParams {
   int G;
   int n_gather;              // groups below this are routed experts
   int64_t ident_row0, n_tokens;
+  // weight mode: each dense group's rows are cut into `pieces` runs of at most
+  // `kchunk` rows (so its tiles take about as long as the routed ones); with
+  // more than one piece, piece q of dense group s writes its partial product
+  // to Cpart + (s * pieces + q) * c_gstride, to be summed afterwards
+  int pieces, kchunk;
+  float* Cpart;
 };
 
 // ---------------------------------------------------------------------------
@@ -124,6 +130,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) 
   // ---- tile decode
   int g, m0, n0, Mlim, Klim;
   int64_t rb;
+  float* Cg = p.C;   // weight mode: this tile's output matrix
   const int ntn = (p.N + BN - 1) / BN;
   if (p.mode == 0) {
     const int32_t* tile_start = p.plan;
@@ -157,14 +164,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) 
   } else {
     const int ntm = (p.M + BM - 1) / BM;
     const int per = ntm * ntn;
-    const int total = per * p.G;
-    const int pxcd = (total + kXcds - 1) / kXcds;
+    // virtual groups: the routed experts, then the pieces of the dense groups;
+    // they are dealt to the XCDs round-robin (XCD x takes x, x + 8, ...), all
+    // tiles of one virtual group on one XCD, so the groups' different lengths
+    // average out over the XCDs and each group's operands share one L2
+    const int nv = p.n_gather + (p.G - p.n_gather) * p.pieces;
     const int slot = blockIdx.x / kXcds;
-    if (slot >= pxcd) return;
-    const int L = (blockIdx.x % kXcds) * pxcd + slot;
-    if (L >= total) return;
-    g = L / per;
-    const int local = L - g * per;
+    const int gl = slot / per;
+    const int gv = (int)(blockIdx.x % kXcds) + kXcds * gl;
+    if (gv >= nv) return;
+    const int local = slot - gl * per;
     // the smaller operand's tiles vary fastest, so it stays in L2 while the
     // larger one streams through once
     if (p.M <= p.N) {
@@ -174,13 +183,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) 
       m0 = (local / ntn) * BM;
       n0 = (local % ntn) * BN;
     }
-    rb = p.plan[p.G + 1 + g];
-    Klim = p.plan[p.G + 1 + p.G + g];
+    if (gv < p.n_gather) {
+      g = gv;
+      rb = p.plan[p.G + 1 + g];
+      Klim = p.plan[p.G + 1 + p.G + g];
+      Cg = p.C + g * p.c_gstride;
+    } else {
+      const int sd = (gv - p.n_gather) / p.pieces, q = (gv - p.n_gather) % p.pieces;
+      g = p.n_gather + sd;
+      rb = p.plan[p.G + 1 + g] + (int64_t)q * p.kchunk;
+      Klim = p.plan[p.G + 1 + p.G + g];
+      if (p.pieces > 1) Klim = min(p.kchunk, Klim - q * p.kchunk);
+      Cg = p.pieces == 1 ? p.Cs + (int64_t)sd * p.c_gstride
+                         : p.Cpart + (int64_t)(sd * p.pieces + q) * p.c_gstride;
+    }
     Mlim = p.M;
     if (Klim <= 0) {
-      // no rows: the gradient of this group's weights is zero
-      float* Cg = g < p.n_gather ? p.C + g * p.c_gstride
-                                 : p.Cs + (int64_t)(g - p.n_gather) * p.c_gstride;
+      // no rows: the gradient of this group's weights (or piece) is zero
       for (int i = tid; i < BM * BN / 4; i += 64 * NW) {
         const int m = m0 + i / (BN / 4), n = n0 + 4 * (i % (BN / 4));
         if (m < p.M && n < p.N)
@@ -406,9 +425,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) 
   // ---- store: acc[i][j] is the 32 x 32 block of C^T; element v of lane
   // (lr, lh) is row 32 i + lr and column 8 (v / 4) + 4 lh + v % 4 of fragment j,
   // so each lane holds runs of 4 consecutive columns
-  float* C = p.C;
-  if (p.mode == 1)
-    C = routed ? p.C + g * p.c_gstride : p.Cs + (int64_t)(g - p.n_gather) * p.c_gstride;
+  float* C = Cg;
   {
     // through LDS (free: run() ended with a barrier after its last reads), one
     // 32-column fragment per pass, so each global store instruction writes
@@ -709,7 +726,35 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict
   *reinterpret_cast<float4*>(dx + t * d + c) = acc;
 }
 
+// out[s][i] = sum over q (in order) of part[s][q][i]; n (a multiple of 4)
+// elements per matrix, P pieces, blockIdx.y = s
+__global__ __launch_bounds__(256) void reduce_pieces_kernel(const float* __restrict__ part,
+                                                            int P, int64_t n,
+                                                            float* __restrict__ out,
+                                                            int64_t out_stride) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  const float* src = part + (int64_t)blockIdx.y * P * n + i;
+  float4 a = *reinterpret_cast<const float4*>(src);
+  for (int q = 1; q < P; ++q) {
+    const float4 b = *reinterpret_cast<const float4*>(src + (int64_t)q * n);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  *reinterpret_cast<float4*>(out + (int64_t)blockIdx.y * out_stride + i) = a;
+}
+
 inline unsigned blocks_of(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+// Dense groups' rows per weight-gradient piece: the experts' (shared) and the
+// router's (whose single group has all N rows).
+constexpr int kExpertChunk = 2048, kRouterChunk = 512, kMaxPieces = 32;
+inline int pieces_of(int64_t N, int chunk) {
+  const int64_t p = (N + chunk - 1) / chunk;
+  return (int)(p < 1 ? 1 : (p > kMaxPieces ? kMaxPieces : p));
+}
+inline int chunk_of(int64_t N, int chunk) {
+  const int P = pieces_of(N, chunk);
+  return (int)(((N + P - 1) / P + 31) / 32 * 32);   // rows per piece, a multiple of 32
+}
 inline int64_t colsum_blocks(int64_t N) {
   const int64_t nb = (N + 255) / 256;
   return nb < 1 ? 1 : (nb > 1024 ? 1024 : nb);
@@ -746,6 +791,14 @@ BwdLayout bwd_ws_layout(const moe_problem* p) {
   L.dz = take(N * E * 4);
   L.dz16 = take(N * Ep * 2);
   L.colsum = take((size_t)colsum_blocks((int64_t)N) * E * 8);
+  {
+    // partial weight gradients of the dense groups' pieces
+    const size_t pe = S ? (size_t)pieces_of((int64_t)N, kExpertChunk) : 0;
+    const size_t pr = (size_t)pieces_of((int64_t)N, kRouterChunk);
+    const size_t a = pe > 1 ? S * pe * d * I : 0;
+    const size_t b = pr > 1 ? pr * E * d : 0;
+    L.part = take((a > b ? a : b) * 4);
+  }
   L.total = off;
   return L;
 }
@@ -785,12 +838,16 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
     if (err != hipSuccess) return err; \
   } while (0)
 
+  auto mark = [&](int i) {
+    if (c.marks[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(c.marks[i]), s);
+  };
   // Row tiles of BM = 256 rows when the groups are large, else 128 (a group
   // of r rows costs ceil(r / BM) tiles).
   const int bm = (R / G >= 512) ? 256 : 128;
   const int bmr = N >= 512 ? 256 : 128;
   // tile plans: experts + shared experts over the forward's row layout, and
   // one dense group of N rows for the router products
+  mark(2 * MOE_BSTAGE_PREP);
   MOE_CHK(launch_ffn_plan(c.offsets, E, S, N, nk, nk, bm, plan, s));
   MOE_CHK(launch_ffn_plan(nullptr, 0, 1, N, 0, 0, bmr, plan_r, s));
   if (S > 0) {
@@ -831,7 +888,9 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
     return Operand{W(r_), W(s_), (int64_t)I * d, ld, 0};
   };
 
+  mark(2 * MOE_BSTAGE_PREP + 1);
   // recompute a = x W_gate^T and u = x W_up^T per row
+  mark(2 * MOE_BSTAGE_RECOMPUTE);
   q.mode = 0;
   q.K = d;
   q.N = I;
@@ -845,17 +904,23 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   q.B = Wop(c.wu, c.su, d);
   q.C = uf;
   MOE_CHK(row_gemm(TN{}, q, row_tiles * tn(I)));
+  mark(2 * MOE_BSTAGE_RECOMPUTE + 1);
   // du_h = dy W_down (W_down [d][I]: the reduction index is its row)
+  mark(2 * MOE_BSTAGE_DH);
   q.A = dyin;
   q.B = Wop(c.wd, c.sd, I);
   q.C = dhu;
   MOE_CHK(row_gemm(TT{}, q, row_tiles * tn(I)));
 
+  mark(2 * MOE_BSTAGE_DH + 1);
+  mark(2 * MOE_BSTAGE_ROWS);
   bwd_rows_kernel<<<(unsigned)R, 256, 0, s>>>(af, uf, dhu, slot, c.topk_w, c.offsets, E, nk, I,
                                               swiglu ? 1 : 0, c.clip, hg, da, du, dgr);
   MOE_CHK(hipGetLastError());
 
+  mark(2 * MOE_BSTAGE_ROWS + 1);
   // weight gradients, one group per expert: K = the group's rows
+  mark(2 * MOE_BSTAGE_WGRAD);
   q.mode = 1;
   const Operand hgin{hg, hg, 0, I, 0};
   const Operand dain{da, da, 0, I, 0};
@@ -863,10 +928,23 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
 #ifndef MOE_BWD_WCFG
 #define MOE_BWD_WCFG 256, 32, 8, 3
 #endif
+  float* part = reinterpret_cast<float*>(base + L.part);
+  q.pieces = S ? pieces_of(N, kExpertChunk) : 1;
+  q.kchunk = S ? chunk_of(N, kExpertChunk) : 0;
+  q.Cpart = part;
+  // launch over the virtual groups (routed experts, then the dense pieces),
+  // then sum the pieces of each dense group
   auto wgemm = [&](const BwdGemmParams& pp, int M, int Nn) {
     constexpr int cfg[4] = {MOE_BWD_WCFG};   // tile rows, k-slice, waves, stages
-    const int64_t tiles = (int64_t)G * ((M + cfg[0] - 1) / cfg[0]) * tn(Nn);
-    return launch_bwd_gemm<1, 1, cfg[0], cfg[1], cfg[2], cfg[3]>(pp, tiles, s);
+    const int nv = pp.n_gather + (pp.G - pp.n_gather) * pp.pieces;
+    const int64_t tiles = (int64_t)(nv + kXcds - 1) / kXcds * kXcds *
+                          ((M + cfg[0] - 1) / cfg[0]) * tn(Nn);
+    hipError_t e = launch_bwd_gemm<1, 1, cfg[0], cfg[1], cfg[2], cfg[3]>(pp, tiles, s);
+    if (e != hipSuccess || pp.pieces == 1 || pp.G == pp.n_gather) return e;
+    const int64_t n = (int64_t)M * Nn;
+    reduce_pieces_kernel<<<dim3(blocks_of(n / 4, 256), (unsigned)(pp.G - pp.n_gather)), 256, 0,
+                           s>>>(pp.Cpart, pp.pieces, n, pp.Cs, pp.c_gstride);
+    return hipGetLastError();
   };
   // dW_down[e] = sum_r dy_t^T (g h_r)   ([d][I])
   q.M = d; q.N = I; q.ldc = I; q.c_gstride = (int64_t)d * I;
@@ -882,7 +960,9 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   q.A = duin; q.C = c.dw_up; q.Cs = c.dws_up;
   MOE_CHK(wgemm(q, I, d));
 
+  mark(2 * MOE_BSTAGE_WGRAD + 1);
   // per-row input gradient dx_r = da W_gate + du W_up ([R][d])
+  mark(2 * MOE_BSTAGE_DX);
   q.mode = 0;
   q.N = d; q.ldc = d; q.K = I; q.K2 = I;
   q.C = dxp; q.Cs = nullptr;
@@ -926,11 +1006,14 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   qr.M = E;
   qr.N = d;
   qr.ldc = d;
-  qr.c_gstride = 0;
   qr.B = Operand{x, x, 0, d, 0};
   qr.C = c.dw_router;
   qr.Cs = c.dw_router;
-  MOE_CHK((launch_bwd_gemm<1, 1, 256>(qr, (int64_t)((E + 255) / 256) * tn(d), s)));
+  qr.c_gstride = (int64_t)E * d;
+  qr.pieces = pieces_of(N, kRouterChunk);
+  qr.kchunk = chunk_of(N, kRouterChunk);
+  qr.Cpart = part;
+  MOE_CHK(wgemm(qr, E, d));
   if (c.d_logit_bias) {
     const int64_t nb = colsum_blocks(N);
     const int64_t chunk = (N + nb - 1) / nb;
@@ -942,6 +1025,7 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   }
   dx_combine_kernel<<<blocks_of(N * d / 4, 256), 256, 0, s>>>(dxp, c.row_of, c.dx, N, d, k, S);
   MOE_CHK(hipGetLastError());
+  mark(2 * MOE_BSTAGE_DX + 1);
 #undef MOE_CHK
   return hipSuccess;
 }

@@ -160,6 +160,7 @@ struct BwdLayout {
   size_t dz;               // f32 [N][E]
   size_t dz16;             // bf16 [N][Ep]  (E rounded up to 8, zero padded)
   size_t colsum;           // f64 [blocks][E]
+  size_t part;             // f32 partial weight gradients of the dense groups' pieces
   size_t total;
 };
 BwdLayout bwd_ws_layout(const moe_problem* p);
@@ -178,6 +179,7 @@ struct BwdCall {
   float *d_logit_bias, *dz_out, *dg_out;       // nullable
   void* ws;
   BwdLayout L;
+  void* marks[2 * MOE_NUM_BSTAGES];            // optional hipEvent_t around each stage
 };
 hipError_t launch_backward(const BwdCall& c, hipStream_t s);
 

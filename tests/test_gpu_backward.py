@@ -232,3 +232,150 @@ def test_backward_rejects_f32():
                    token_of_row=fake)
     gr = L.grads(dx=fake, dw_router=fake, dw_up=fake, dw_down=fake)
     assert L.moe_backward(p, wts, fake, rt, fake, gr, fake, raw=True) == -3
+
+
+FULL = ["cap", "mix-D", "ds-D", "mix-P", "ds-P", "v41"]
+
+
+def _oracle_token_grads(w, ors, route, disp, dy, toks):
+    """dx, dg (k) and dz (E) of the tokens toks from the oracle's pieces: each
+    expert on the sampled rows it keeps (expert_ffn for dg, expert_ffn_backward
+    for dx), the shared experts, the gate-weight gradient and the router
+    product.  Each expert's weights are built once."""
+    idx = route["idx"][toks]
+    row_of = disp["row_of"][toks]
+    g = O.gate_weights(route["s"][toks], idx, w.renormalize)
+    x = ors.x[toks]
+    dyt = dy[toks].astype(np.float64)
+    n = len(toks)
+    dx = np.zeros((n, w.d))
+    dg = np.zeros((n, w.k))
+    for e in np.unique(idx[row_of >= 0]):
+        r, j = np.nonzero((idx == e) & (row_of >= 0))
+        wg, wu, wd = ors.expert(int(e))
+        out = O.expert_ffn(x[r], wg, wu, wd, w.activation, w.clip)
+        dg[r, j] = np.sum(dyt[r] * out, axis=1)
+        dxe, *_ = O.expert_ffn_backward(x[r], wg, wu, wd, w.activation, w.clip,
+                                        g[r, j][:, None] * dyt[r])
+        np.add.at(dx, r, dxe)
+    for s_ in range(w.S):
+        wg, wu, wd = ors.shared(s_)
+        dxs, *_ = O.expert_ffn_backward(x, wg, wu, wd, w.activation, w.clip, dyt)
+        dx += dxs
+    dz = O.gate_backward(route["s"][toks], route["z"][toks], idx, dg, w.gating, w.renormalize)
+    dx += dz @ ors.wr
+    return dx, dg, dz
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_backward_sampled(name):
+    """The backward at the full workload sizes, in the configuration bench.py
+    --backward times, checked on samples the oracle computes piece by piece:
+    the weight gradients of a few experts restricted to a random subset of
+    hidden units (an FFN restricted to some units is exactly those units of
+    the whole FFN, so the oracle's expert backward on the restricted weights
+    gives those rows of dW_gate / dW_up and columns of dW_down), and dx, dg, dz
+    of tokens spread over the batch.  The router gradients are checked as the
+    products they are of the GPU's own dz (dW_router = dz^T x, d_logit_bias =
+    sum_t dz_t) in float64."""
+    import parity
+    from mixture_experts_layer_16_amd import _lib as L
+    w = synth.get(name)
+    _say(f"[bwd-full] {name}: generating inputs")
+    inp = synth.make_inputs(w)
+    di = sdev.upload(inp)
+    y, out = parity.gpu_forward(w, di)
+    del y
+    g = parity.to_np(out)
+    ors = parity.OracleSide(inp)
+    route = ors.route()
+    N, d, E, k, I, S = w.N, w.d, w.E, w.k, w.I, w.S
+    gidx = g["topk_idx"][: N * k].reshape(N, k)
+    assert np.array_equal(gidx, route["idx"]), "near-tie routing"
+    disp = O.dispatch(route["idx"], E, O.capacity(w.f, N, k, E))
+    assert np.array_equal(g["row_of"][: N * k].reshape(N, k), disp["row_of"])
+    dy = synth.upstream_grad(w)
+    _say(f"[bwd-full] {name}: backward on the GPU")
+    dev = di.x.device
+    f32 = torch.float32
+    swiglu = w.activation == "swiglu"
+    t = dict(dx=torch.empty((N, d), dtype=f32, device=dev),
+             dw_router=torch.empty((E, d), dtype=f32, device=dev),
+             dw_up=torch.empty((E, I, d), dtype=f32, device=dev),
+             dw_down=torch.empty((E, d, I), dtype=f32, device=dev),
+             d_logit_bias=torch.empty(E, dtype=f32, device=dev),
+             dz=torch.empty(N * E, dtype=f32, device=dev),
+             dg=torch.empty(N * k, dtype=f32, device=dev))
+    if swiglu:
+        t["dw_gate"] = torch.empty((E, I, d), dtype=f32, device=dev)
+    if S:
+        t["dws_up"] = torch.empty((S, I, d), dtype=f32, device=dev)
+        t["dws_down"] = torch.empty((S, d, I), dtype=f32, device=dev)
+        if swiglu:
+            t["dws_gate"] = torch.empty((S, I, d), dtype=f32, device=dev)
+    wts = L.weights(di.w_router, di.w_gate, di.w_up, di.w_down, di.ws_gate, di.ws_up,
+                    di.ws_down)
+    rt = L.routing(**{n: v for n, v in out.items() if v is not None})
+    dyt = torch.from_numpy(dy).to(dev)
+    L.moe_backward(parity.problem_of(w), wts, di.x, rt, dyt, L.grads(**t),
+                   L.backward_workspace(parity.problem_of(w)))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    rep = {}
+    # -- expert weight gradients on a subset of hidden units
+    U = np.sort(rng.choice(I, size=min(I, 48), replace=False))
+    Ut = torch.from_numpy(U).to(dev)
+    rows_per_e = np.diff(g["offsets"])
+    busiest = int(np.argmax(rows_per_e))
+    others = [e for e in rng.permutation(E) if rows_per_e[e] > 0 and e != busiest][:1]
+    g_all = O.gate_weights(route["s"], route["idx"], w.renormalize)
+    worst = 0.0
+    for e in [busiest] + others + [("s", s_) for s_ in range(S)]:
+        if isinstance(e, tuple):
+            toks = np.arange(N)
+            d_out = dy.astype(np.float64)
+            wg, wu, wd = ors.shared(e[1])
+            pre = "dws_"
+            ei = e[1]
+        else:
+            toks, slot = np.nonzero((route["idx"] == e) & (disp["row_of"] >= 0))
+            d_out = g_all[toks, slot][:, None] * dy[toks].astype(np.float64)
+            wg, wu, wd = ors.expert(e)
+            pre = "dw_"
+            ei = e
+        wgU = None if wg is None else wg[U]
+        _, rg, ru, rd = O.expert_ffn_backward(ors.x[toks], wgU, wu[U], wd[:, U], w.activation,
+                                              w.clip, d_out)
+        got = {"up": t[pre + "up"][ei].index_select(0, Ut).cpu().numpy(),
+               "down": t[pre + "down"][ei].index_select(1, Ut).cpu().numpy()}
+        ref = {"up": ru, "down": rd}
+        if swiglu:
+            got["gate"] = t[pre + "gate"][ei].index_select(0, Ut).cpu().numpy()
+            ref["gate"] = rg
+        for n_ in got:
+            r_, mx, _ = _rel(got[n_], ref[n_])
+            rep[f"{pre}{n_}[{ei}]"] = round(r_, 5)
+            worst = max(worst, r_)
+            assert r_ <= RMS_TOL and mx <= MAX_TOL, (name, e, n_, r_, mx)
+    # -- dx, dg, dz of sampled tokens
+    toks = np.unique(np.linspace(0, N - 1, min(N, 12)).astype(np.int64))
+    Tt = torch.from_numpy(toks).to(dev)
+    gdx = t["dx"].index_select(0, Tt).cpu().numpy()
+    gdz = t["dz"].view(N, E).index_select(0, Tt).cpu().numpy()
+    gdg = t["dg"].view(N, k).index_select(0, Tt).cpu().numpy()
+    rdx, rdg, rdz = _oracle_token_grads(w, ors, route, disp, dy, toks)
+    for n_, a, b in (("dx", gdx, rdx), ("dg", gdg, rdg), ("dz", gdz, rdz)):
+        r_, mx, grp = _rel(a, b, n_ == "dx")
+        rep[n_] = round(r_, 5)
+        assert r_ <= RMS_TOL and mx <= MAX_TOL and grp <= GROUP_RMS_TOL, (name, n_, r_, mx, grp)
+    # -- router gradients: products of the GPU's own dz
+    dz_all = t["dz"].view(N, E).double()
+    x64 = torch.from_numpy(ors.x).to(dev)
+    ref_wr = (dz_all.t() @ x64).cpu().numpy()
+    r_, mx, _ = _rel(t["dw_router"].cpu().numpy(), ref_wr)
+    rep["dw_router_vs_own_dz"] = round(r_, 5)
+    assert r_ <= RMS_TOL and mx <= MAX_TOL
+    ref_lb = dz_all.sum(0).cpu().numpy()
+    glb = t["d_logit_bias"].cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(glb - ref_lb)) <= 1e-5 * max(np.max(np.abs(ref_lb)), 1e-30) + 1e-6
+    _say(f"[bwd-full] {name}: {rep}")

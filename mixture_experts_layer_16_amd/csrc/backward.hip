@@ -25,6 +25,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
@@ -451,8 +452,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) 
         const float4 v = *reinterpret_cast<const float4*>(eb + row * PS + c4 * 16);
         const int m = m0 + wm * WROWS + row;
         const int n = n0 + wn * WCOLS + 32 * j + 4 * c4;
+        // non-temporal: the results are not read again by this kernel
+        // (measured: about 1% less time for the backward)
         if (m < Mlim && n < p.N)
-          *reinterpret_cast<float4*>(C + (p.mode == 0 ? rb + m : (int64_t)m) * p.ldc + n) = v;
+          __builtin_nontemporal_store(
+              f32x4_t{v.x, v.y, v.z, v.w},
+              reinterpret_cast<f32x4_t*>(C + (p.mode == 0 ? rb + m : (int64_t)m) * p.ldc + n));
       }
     }
   }

@@ -194,8 +194,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--backward", action="store_true",
-                    help="time the backward pass (moe_backward on the forward's routing) "
-                         "instead of the forward")
+                    help="time the backward pass (moe_backward on the forward's routing and "
+                         "saved pre-activations) instead of the forward")
+    ap.add_argument("--recompute", action="store_true",
+                    help="with --backward: the forward saves no pre-activations, the backward "
+                         "recomputes them")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the run, copy 256 MiB device-to-device once: a kernel of known "
                          "traffic to scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
@@ -353,7 +356,8 @@ def main():
 
 
 def bench_backward(args, w, inp, di, p):
-    """The backward pass: forward once for the routing, then K timed calls of
+    """The backward pass: forward once for the routing (and, unless
+    --recompute, the saved pre-activations), then K timed calls of
     moe_backward (all gradients: x, every expert, shared experts, router,
     logit offset).  Dominant stage: the three weight-gradient grouped GEMMs."""
     import numpy as np
@@ -370,6 +374,12 @@ def bench_backward(args, w, inp, di, p):
                 row_of=torch.empty(N * k, dtype=i32, device=dev),
                 token_of_row=torch.empty(N * k, dtype=i32, device=dev),
                 logits=torch.empty(N * E, dtype=torch.float64, device=dev))
+    swiglu = w.activation == "swiglu"
+    if not args.recompute:
+        # the training forward keeps x W_gate^T and x W_up^T (fp16) for the backward
+        rt_t["act_u"] = torch.empty((N * (k + S), I), dtype=torch.float16, device=dev)
+        if swiglu:
+            rt_t["act_a"] = torch.empty((N * (k + S), I), dtype=torch.float16, device=dev)
     wts = L.weights(di.w_router, di.w_gate, di.w_up, di.w_down, di.ws_gate, di.ws_up, di.ws_down)
     rt = L.routing(**rt_t)
     ws = L.workspace(p)
@@ -377,7 +387,6 @@ def bench_backward(args, w, inp, di, p):
     L.moe_forward(p, wts, di.x, di.logit_bias, di.sel_bias, di.modality, y, rt, ws)
     torch.cuda.synchronize()
     del ws, y
-    swiglu = w.activation == "swiglu"
     g = dict(dx=torch.empty((N, d), dtype=f32, device=dev),
              dw_router=torch.empty((E, d), dtype=f32, device=dev),
              dw_up=torch.empty((E, I, d), dtype=f32, device=dev),
@@ -476,7 +485,9 @@ def bench_backward(args, w, inp, di, p):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; random-init weights of the stated shapes; dy ~ N(0, 1))",
-        "config": {"workload": w.name, "pass": "backward", "N": N, "d": d, "E": E, "S": S,
+        "config": {"workload": w.name, "pass": "backward",
+                   "activations": "recomputed" if args.recompute else "saved by the forward",
+                   "N": N, "d": d, "E": E, "S": S,
                    "k": k, "I": I, "capacity_factor": w.f, "gating": w.gating,
                    "activation": w.activation, "kept_assignments": A},
         "layer": {"tflops": flops / (ms_step * 1e-3) / 1e12,

@@ -132,6 +132,15 @@ typedef struct {
   double* logits;            /* [N][E] router logits z (float64) */
   int32_t* final_idx;        /* [N*k] expert that processes each slot (the rerouted
                                 one under MOE_OVERFLOW_REROUTE), -1 if dropped */
+  /* Pre-activations of the expert FFNs, for moe_backward (MOE_BF16 only; both
+   * or neither for SwiGLU, act_u alone for ReLU): IEEE fp16 [N*k + N*S][I],
+   * 16-byte aligned, in the layer's row layout (routed rows [0, offsets[E]),
+   * then N rows per shared expert from row N*k).  act_a = x W_gate^T,
+   * act_u = x W_up^T (SwiGLU) or x W1 before the ReLU.  Written by moe_forward /
+   * moe_forward_ex / moe_forward_routed when given; read by moe_backward, which
+   * then skips recomputing them. */
+  void* act_a;
+  void* act_u;
 } moe_routing;
 
 /* Bytes of device workspace any call below needs for problem p (host). */
@@ -342,7 +351,9 @@ int moe_backward_workspace_size(const moe_problem* p, size_t* bytes);
  *   w        the forward's weights (w_router required)
  *   routing  (host struct of device pointers) from the moe_forward call:
  *            topk_idx, topk_w, logits, offsets, row_of, token_of_row required
- *            (moe_forward writes them when they are given in routing_out)
+ *            (moe_forward writes them when they are given in routing_out);
+ *            act_a / act_u optional: the forward's saved pre-activations, used
+ *            instead of recomputing x W_gate^T and x W_up^T
  *   dy       (device) float32 [N][d], gradient of the output y
  *   grads    (host struct of device pointers) outputs, overwritten
  *   ws       (device) moe_backward_workspace_size() bytes

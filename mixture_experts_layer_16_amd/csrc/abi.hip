@@ -150,6 +150,17 @@ static int check_route_inputs(const moe_problem* p, const void* x, const void* w
   return MOE_OK;
 }
 
+// Saved pre-activations (moe_routing.act_a / act_u): bf16 layers only; SwiGLU
+// takes both or neither, ReLU act_u alone; 16-byte aligned.
+static int check_acts(const moe_problem* p, const moe_routing* r) {
+  if (!r->act_a && !r->act_u) return MOE_OK;
+  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (p->activation == MOE_SWIGLU && (!r->act_a || !r->act_u)) return MOE_ERR_NULL;
+  if (p->activation == MOE_RELU && (r->act_a || !r->act_u)) return MOE_ERR_INVALID;
+  if (!aligned16(r->act_u) || (r->act_a && !aligned16(r->act_a))) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -380,6 +391,10 @@ static int forward_impl(const moe_problem* p, const moe_weights* w, const void* 
       if (q && !aligned16(q)) return MOE_ERR_UNSUPPORTED;
   }
   if (routing_out && routing_out->modality_counts && !modality) return MOE_ERR_NULL;
+  if (routing_out) {
+    st = check_acts(p, routing_out);
+    if (st) return st;
+  }
   const WsLayout L = ws_layout(p);
   if (!ws) return MOE_ERR_NULL;
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -461,6 +476,8 @@ static int forward_impl(const moe_problem* p, const moe_weights* w, const void* 
   c.h = base + L.h;
   c.y_rows = base + L.yrows;
   c.plan = reinterpret_cast<int32_t*>(base + L.plan);
+  c.save_a = r.act_a;
+  c.save_u = r.act_u;
   if (prof) {
     for (int i = 0; i < 6; ++i) c.marks[i] = prof->ev[2 * MOE_STAGE_PLAN + i];
   }
@@ -522,6 +539,8 @@ int moe_backward_ex(const moe_problem* p, const moe_weights* w, const void* x,
   const moe_routing& r = *routing;
   if (!r.topk_idx || !r.topk_w || !r.logits || !r.offsets || !r.row_of || !r.token_of_row)
     return MOE_ERR_NULL;
+  st = check_acts(p, &r);
+  if (st) return st;
   const moe_grads& g = *grads;
   if (!g.dx || !g.dw_router || !g.dw_up || !g.dw_down || (swiglu && !g.dw_gate))
     return MOE_ERR_NULL;
@@ -560,6 +579,8 @@ int moe_backward_ex(const moe_problem* p, const moe_weights* w, const void* x,
   c.offsets = r.offsets;
   c.row_of = r.row_of;
   c.token_of_row = r.token_of_row;
+  c.act_a = static_cast<const uint16_t*>(r.act_a);
+  c.act_u = static_cast<const uint16_t*>(r.act_u);
   c.dx = g.dx;
   c.dw_router = g.dw_router;
   c.dw_gate = g.dw_gate; c.dw_up = g.dw_up; c.dw_down = g.dw_down;

@@ -543,8 +543,10 @@ __global__ __launch_bounds__(256) void slot_of_row_kernel(const int32_t* __restr
 //   dh = g du_h, zero where the clamp is active
 //   da = dh u silu'(a), du = dh silu(a)   (ReLU: du = dh [u > 0])
 // writes g h, da, du as bf16 and dg_r as float32.
+template <bool SAVED>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(
-    const float* __restrict__ af, const float* __restrict__ uf, const float* __restrict__ dhu,
+    const float* __restrict__ af, const float* __restrict__ uf, const uint16_t* __restrict__ a16,
+    const uint16_t* __restrict__ u16, const float* __restrict__ dhu,
     const int32_t* __restrict__ slot, const float* __restrict__ topk_w,
     const int32_t* __restrict__ offsets, int E, int64_t routed_rows, int I, int swiglu,
     float clip, uint16_t* __restrict__ hg, uint16_t* __restrict__ da, uint16_t* __restrict__ du,
@@ -558,14 +560,27 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
   const int64_t o = r * (int64_t)I;
   float part = 0.f;
   for (int i = 4 * threadIdx.x; i < I; i += 4 * 256) {
-    const float4 u4 = *reinterpret_cast<const float4*>(uf + o + i);
     const float4 d4 = *reinterpret_cast<const float4*>(dhu + o + i);
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    if (swiglu) {
-      const float4 a4 = *reinterpret_cast<const float4*>(af + o + i);
-      a[0] = a4.x; a[1] = a4.y; a[2] = a4.z; a[3] = a4.w;
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, u[4];
+    if (SAVED) {
+      // the forward's fp16 pre-activations; an infinite u marks an element
+      // the forward clamped (sign(u) sign(a) = sign of the clamped h)
+      const uint2 u2 = *reinterpret_cast<const uint2*>(u16 + o + i);
+      u[0] = f16_to_f32(u2.x & 0xffffu); u[1] = f16_to_f32(u2.x >> 16);
+      u[2] = f16_to_f32(u2.y & 0xffffu); u[3] = f16_to_f32(u2.y >> 16);
+      if (swiglu) {
+        const uint2 a2 = *reinterpret_cast<const uint2*>(a16 + o + i);
+        a[0] = f16_to_f32(a2.x & 0xffffu); a[1] = f16_to_f32(a2.x >> 16);
+        a[2] = f16_to_f32(a2.y & 0xffffu); a[3] = f16_to_f32(a2.y >> 16);
+      }
+    } else {
+      const float4 u4 = *reinterpret_cast<const float4*>(uf + o + i);
+      u[0] = u4.x; u[1] = u4.y; u[2] = u4.z; u[3] = u4.w;
+      if (swiglu) {
+        const float4 a4 = *reinterpret_cast<const float4*>(af + o + i);
+        a[0] = a4.x; a[1] = a4.y; a[2] = a4.z; a[3] = a4.w;
+      }
     }
-    const float u[4] = {u4.x, u4.y, u4.z, u4.w};
     const float dh_u[4] = {d4.x, d4.y, d4.z, d4.w};
     uint16_t ohg[4], oda[4], odu[4];
 #pragma unroll
@@ -574,12 +589,19 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
       if (swiglu) {
         const float sg = 1.f / (1.f + expf(-a[q]));
         const float act = a[q] * sg;
-        const float hpre = act * u[q];
-        const bool pass = !(clip > 0.f) || fabsf(hpre) <= clip;
-        h = clip > 0.f ? fminf(fmaxf(hpre, -clip), clip) : hpre;
+        bool pass;
+        if (SAVED) {
+          // the forward's own clamp decision (see the comment above)
+          pass = !__builtin_isinf(u[q]);
+          h = pass ? act * u[q] : ((u[q] < 0.f) != __builtin_signbit(a[q]) ? -clip : clip);
+        } else {
+          const float hpre = act * u[q];
+          pass = !(clip > 0.f) || fabsf(hpre) <= clip;
+          h = clip > 0.f ? fminf(fmaxf(hpre, -clip), clip) : hpre;
+        }
         dh = pass ? g * dh_u[q] : 0.f;
-        dU = dh * act;
-        dA = dh * u[q] * (sg * (1.f + a[q] * (1.f - sg)));
+        dU = pass ? dh * act : 0.f;
+        dA = pass ? dh * u[q] * (sg * (1.f + a[q] * (1.f - sg))) : 0.f;
       } else {
         h = fmaxf(u[q], 0.f);
         dh = g * dh_u[q];
@@ -894,21 +916,25 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   };
 
   mark(2 * MOE_BSTAGE_PREP + 1);
-  // recompute a = x W_gate^T and u = x W_up^T per row
+  // recompute a = x W_gate^T and u = x W_up^T per row (unless the forward
+  // saved them)
   mark(2 * MOE_BSTAGE_RECOMPUTE);
+  const bool saved = c.act_u != nullptr;
   q.mode = 0;
   q.K = d;
   q.N = I;
   q.ldc = I;
   q.A = xin;
-  if (swiglu) {
-    q.B = Wop(c.wg, c.sg, d);
-    q.C = af;
+  if (!saved) {
+    if (swiglu) {
+      q.B = Wop(c.wg, c.sg, d);
+      q.C = af;
+      MOE_CHK(row_gemm(TN{}, q, row_tiles * tn(I)));
+    }
+    q.B = Wop(c.wu, c.su, d);
+    q.C = uf;
     MOE_CHK(row_gemm(TN{}, q, row_tiles * tn(I)));
   }
-  q.B = Wop(c.wu, c.su, d);
-  q.C = uf;
-  MOE_CHK(row_gemm(TN{}, q, row_tiles * tn(I)));
   mark(2 * MOE_BSTAGE_RECOMPUTE + 1);
   // du_h = dy W_down (W_down [d][I]: the reduction index is its row)
   mark(2 * MOE_BSTAGE_DH);
@@ -919,8 +945,14 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
 
   mark(2 * MOE_BSTAGE_DH + 1);
   mark(2 * MOE_BSTAGE_ROWS);
-  bwd_rows_kernel<<<(unsigned)R, 256, 0, s>>>(af, uf, dhu, slot, c.topk_w, c.offsets, E, nk, I,
-                                              swiglu ? 1 : 0, c.clip, hg, da, du, dgr);
+  if (saved)
+    bwd_rows_kernel<true><<<(unsigned)R, 256, 0, s>>>(af, uf, c.act_a, c.act_u, dhu, slot,
+                                                      c.topk_w, c.offsets, E, nk, I,
+                                                      swiglu ? 1 : 0, c.clip, hg, da, du, dgr);
+  else
+    bwd_rows_kernel<false><<<(unsigned)R, 256, 0, s>>>(af, uf, nullptr, nullptr, dhu, slot,
+                                                       c.topk_w, c.offsets, E, nk, I,
+                                                       swiglu ? 1 : 0, c.clip, hg, da, du, dgr);
   MOE_CHK(hipGetLastError());
 
   mark(2 * MOE_BSTAGE_ROWS + 1);

@@ -149,6 +149,19 @@ __device__ __forceinline__ float swiglu(float a, float u, float clip) {
   return h;
 }
 
+// The saved up pre-activation (fp16 bits) of a SwiGLU element: u itself, or,
+// where this forward clamped silu(a) u (same formula as swiglu above), an
+// infinity whose sign times the sign of a is the sign of the clamped h -- so
+// the backward follows this pass's clamp decision exactly instead of
+// re-deciding it from fp16-rounded values.
+__device__ __forceinline__ uint16_t saved_up_bits(float a, float u, float clip) {
+  if (clip > 0.f) {
+    const float h = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * u;
+    if (fabsf(h) > clip) return ((h < 0.f) != (a < 0.f)) ? 0xFC00u : 0x7C00u;
+  }
+  return f32_to_f16_sat(u);
+}
+
 struct GemmParams {
   const void* A;                 // x (gate/up) or h (down)
   const int32_t* token_of_row;   // routed groups of the gate/up pass
@@ -166,6 +179,11 @@ struct GemmParams {
   int64_t ident_row0;            // first row of the dense groups (token t of dense
                                  // group i is row ident_row0 + i*n_tokens + t)
   float clip;
+  // gate/up pass, optional (both or neither): the pre-activations written next
+  // to h in the same row layout, fp16 -- Sa = x W_gate^T (SwiGLU), Su = x W_up^T
+  // (SwiGLU) or x W1 before the ReLU
+  void* Sa;
+  void* Su;
 };
 
 // ---------------------------------------------------------------------------
@@ -460,6 +478,10 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
             const float a = acc[i][jn][v];
             const float u = acc[i][jn + FN / 2][v];
             crow[col] = f32_to_f16_sat(swiglu(a, u, p.clip));
+            if (p.Su) {
+              static_cast<uint16_t*>(p.Sa)[(tl.rb + m) * p.ldC + col] = f32_to_f16_sat(a);
+              static_cast<uint16_t*>(p.Su)[(tl.rb + m) * p.ldC + col] = saved_up_bits(a, u, p.clip);
+            }
           }
         }
       } else {
@@ -468,6 +490,8 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
           const int col = tl.n0 + wn * WCOLS + 32 * jn + lr;
           if (col < p.Ncols) {
             float vv = acc[i][jn][v];
+            if (MODE == MODE_RELU_UP && p.Su)
+              static_cast<uint16_t*>(p.Su)[(tl.rb + m) * p.ldC + col] = f32_to_f16_sat(vv);
             if (MODE == MODE_RELU_UP) vv = fmaxf(vv, 0.f);
             crow[col] = f32_to_f16_sat(vv);
           }
@@ -807,7 +831,11 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
     constexpr int RDS = WROWS * HC * 2 / 1024;   // 16-byte reads per lane per pass
     static_assert(NW * WROWS * PS <= NS * SB, "epilogue staging fits the stages");
     char* eb = lds + wave * (WROWS * PS);
-    uint16_t* C = static_cast<uint16_t*>(p.C);
+    // WHAT: 0 = the pass's output (h or the expert row); 1 = the gate
+    // pre-activation a (SwiGLU) or the up pre-activation before the ReLU;
+    // 2 = the up pre-activation u (SwiGLU)
+    auto emit = [&](auto WHAT, uint16_t* C) {
+    constexpr int kWhat = decltype(WHAT)::value;
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
 #pragma unroll
@@ -816,19 +844,22 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int vq = 0; vq < 4; ++vq) {
-            float h[4];
+            uint32_t hb[4];   // fp16 bits
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               if (MODE == MODE_GATEUP) {
-                h[c] = swiglu(acc[i][jj][4 * vq + c], acc[i][jj + 2][4 * vq + c], p.clip);
+                const float a = acc[i][jj][4 * vq + c], u = acc[i][jj + 2][4 * vq + c];
+                hb[c] = kWhat == 0 ? f32_to_f16_sat(swiglu(a, u, p.clip))
+                                   : (kWhat == 1 ? f32_to_f16_sat(a) : saved_up_bits(a, u, p.clip));
               } else {
-                h[c] = acc[i][2 * pass + jj][4 * vq + c];
-                if (MODE == MODE_RELU_UP) h[c] = fmaxf(h[c], 0.f);
+                float h = acc[i][2 * pass + jj][4 * vq + c];
+                if (MODE == MODE_RELU_UP && kWhat == 0) h = fmaxf(h, 0.f);
+                hb[c] = f32_to_f16_sat(h);
               }
             }
             uint2 pk;
-            pk.x = (uint32_t)f32_to_f16_sat(h[0]) | ((uint32_t)f32_to_f16_sat(h[1]) << 16);
-            pk.y = (uint32_t)f32_to_f16_sat(h[2]) | ((uint32_t)f32_to_f16_sat(h[3]) << 16);
+            pk.x = hb[0] | (hb[1] << 16);
+            pk.y = hb[2] | (hb[3] << 16);
             *reinterpret_cast<uint2*>(eb + (32 * i + lr) * PS + (32 * jj + 8 * vq + 4 * lh) * 2) =
                 pk;
           }
@@ -843,6 +874,18 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
         const int col = tl.n0 + wn * WCOLS + pass * HC + c8 * 8;
         if (m < tl.M && col < p.Ncols)
           *reinterpret_cast<u32x4_t*>(C + (tl.rb + m) * p.ldC + col) = val;
+      }
+    }
+    };
+    emit(std::integral_constant<int, 0>{}, static_cast<uint16_t*>(p.C));
+    if (MODE != MODE_DOWN && p.Su) {
+      // the pre-activations, for a backward pass (same staging, one more pass
+      // each; the LDS operations of one wave complete in order)
+      if constexpr (MODE == MODE_GATEUP) {
+        emit(std::integral_constant<int, 1>{}, static_cast<uint16_t*>(p.Sa));
+        emit(std::integral_constant<int, 2>{}, static_cast<uint16_t*>(p.Su));
+      } else {
+        emit(std::integral_constant<int, 1>{}, static_cast<uint16_t*>(p.Su));
       }
     }
   }
@@ -1115,6 +1158,8 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   up.ident_row0 = c.identity_row0;
   up.clip = c.clip;
   up.C = c.h;
+  up.Sa = c.save_a;
+  up.Su = c.save_u;
   if (c.activation == MOE_SWIGLU) {
     up.Br0 = c.wg; up.Br1 = c.wu; up.Bs0 = c.sg; up.Bs1 = c.su;
   } else {

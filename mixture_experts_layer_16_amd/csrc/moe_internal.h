@@ -132,6 +132,7 @@ struct FfnCall {
   void* y_rows;                // [rows][d]
   int32_t* plan;               // workspace for the tile plan
   void* marks[6];              // optional hipEvent_t: before/after plan, gate/up, down
+  void *save_a, *save_u;       // optional fp16 [rows][I] pre-activations (bf16 path)
 };
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
 // The tile plan alone (BM-row tiles, no remainder plan), for other grouped GEMMs.
@@ -175,6 +176,7 @@ struct BwdCall {
   const double* logits;                        // [N][E]
   const int32_t *topk_idx, *offsets, *row_of, *token_of_row;
   const float* topk_w;
+  const uint16_t *act_a, *act_u;               // optional fp16 saved pre-activations
   float *dx, *dw_router, *dw_gate, *dw_up, *dw_down, *dws_gate, *dws_up, *dws_down;
   float *d_logit_bias, *dz_out, *dg_out;       // nullable
   void* ws;

@@ -306,3 +306,37 @@ def test_backward_workspace_grows_with_tokens(L):
 def test_grads_struct_matches_the_header_layout(L):
     assert ctypes.sizeof(L.Grads) == 11 * 8
     assert L.Grads.dg.offset == 80
+
+
+def test_saved_activation_pointers_are_validated(L):
+    fake = 0x10000
+    lib = L.LIB
+    B = ctypes.byref
+    w = L.Weights(fake, fake, fake, fake, fake, fake, fake)
+
+    def fwd(p, **acts):
+        r = L.Routing(**acts)
+        return lib.moe_forward(B(p), B(w), fake, None, None, None, fake, B(r), fake, 1 << 40,
+                               None)
+
+    p = L.problem(64, 128, 8, 2, 64, S=1)
+    assert fwd(p, act_a=fake) == -1                      # SwiGLU needs both
+    assert fwd(p, act_u=fake) == -1
+    assert fwd(p, act_a=fake, act_u=fake + 8) == -3      # 16-byte alignment
+    assert fwd(L.problem(64, 128, 8, 2, 64, S=1, dtype="f32"), act_a=fake, act_u=fake) == -3
+    pr = L.problem(64, 128, 8, 2, 64, S=1, activation="relu")
+    wr = L.Weights(fake, None, fake, fake, None, fake, fake)
+    r = L.Routing(act_a=fake, act_u=fake)
+    assert lib.moe_forward(B(pr), B(wr), fake, None, None, None, fake, B(r), fake, 1 << 40,
+                           None) == -2                   # ReLU has no gate pre-activation
+    # the backward checks them the same way
+    rb = L.Routing(topk_idx=fake, topk_w=fake, logits=fake, offsets=fake, row_of=fake,
+                   token_of_row=fake, act_a=fake)
+    g = L.Grads(dx=fake, dw_router=fake, dw_gate=fake, dw_up=fake, dw_down=fake, dws_gate=fake,
+                dws_up=fake, dws_down=fake)
+    assert lib.moe_backward(B(p), B(w), fake, B(rb), fake, B(g), fake, 1 << 40, None) == -1
+
+
+def test_routing_struct_matches_the_header_layout(L):
+    assert ctypes.sizeof(L.Routing) == 12 * 8
+    assert L.Routing.act_u.offset == 88

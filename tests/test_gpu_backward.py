@@ -113,11 +113,30 @@ def oracle_backward(w, ors, dy):
                       overflow=w.overflow)
 
 
-def check_backward(w, inp=None):
+def forward_saving(w, di):
+    """moe_forward with the pre-activations saved (act_a / act_u, fp16)."""
+    from mixture_experts_layer_16_amd import _lib as L
+    import parity
+    p = parity.problem_of(w)
+    out = parity.alloc_routing(w, di.x.device)
+    rows = max(1, w.N * (w.k + w.S))
+    out["act_u"] = torch.full((rows, w.I), float("nan"), dtype=torch.float16, device=di.x.device)
+    out["act_a"] = (torch.full((rows, w.I), float("nan"), dtype=torch.float16, device=di.x.device)
+                    if w.activation == "swiglu" else None)
+    y = torch.full((max(1, w.N), w.d), float("nan"), dtype=torch.float32, device=di.x.device)
+    r = L.routing(**{k: v for k, v in out.items() if v is not None})
+    L.moe_forward(p, L.weights(di.w_router, di.w_gate, di.w_up, di.w_down, di.ws_gate, di.ws_up,
+                               di.ws_down),
+                  di.x, di.logit_bias, di.sel_bias, di.modality, y, r, L.workspace(p))
+    torch.cuda.synchronize()
+    return y, out
+
+
+def check_backward(w, inp=None, saved=False):
     import parity
     inp = inp or synth.make_inputs(w)
     di = sdev.upload(inp)
-    y, out = parity.gpu_forward(w, di)
+    y, out = forward_saving(w, di) if saved else parity.gpu_forward(w, di)
     g = parity.to_np(out)
     ors = parity.OracleSide(inp)
     rep = {}
@@ -162,6 +181,7 @@ def check_backward(w, inp=None):
         assert rep["dz_rowsum"] <= 1e-4 * E
     rep["dropped"] = int(dropped.sum())
     rep["empty_experts"] = int((rows_per_e == 0).sum())
+    rep["saved"] = saved
     _say(f"[backward] {w.name} {rep}")
     bad = {n: v for n, v in errs.items()
            if not (v[0] <= RMS_TOL and v[1] <= MAX_TOL and v[2] <= GROUP_RMS_TOL)}
@@ -172,6 +192,84 @@ def check_backward(w, inp=None):
 @pytest.mark.parametrize("name", ["cap-s", "mix-s", "ds-s", "v41-s", "relu-bf16-s", "mixd-s"])
 def test_backward_families(name):
     check_backward(synth.get(name))
+
+
+@pytest.mark.parametrize("name", ["cap-s", "mix-s", "ds-s", "v41-s", "relu-bf16-s", "mixd-s"])
+def test_backward_with_saved_activations(name):
+    """The forward saves x W_gate^T and x W_up^T (fp16); the backward reads them
+    instead of recomputing.  fp16 rounding (2^-11) is far below the bf16
+    operand rounding the tolerance covers."""
+    check_backward(synth.get(name), saved=True)
+
+
+def _workload(name):
+    # v41-clip-s: the V4.1-shaped small layer with the clip lowered to 0.06 so
+    # that about 30% of silu(a) u are clamped (at 10, none are in the small
+    # layer)
+    if name == "v41-clip-s":
+        return synth.derive(synth.get("v41-s"), name=name, clip=0.06)
+    return synth.get(name)
+
+
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_with_the_clamp_active(saved):
+    check_backward(_workload("v41-clip-s"), saved=saved)
+
+
+@pytest.mark.parametrize("name", ["cap-s", "ds-s", "v41-s", "v41-clip-s", "relu-bf16-s", "mixd-s"])
+def test_saved_activations_match_the_oracle(name):
+    """The saved pre-activations, row by row, against x W^T in float64 (fp16
+    storage: |err| <= 2^-10 |a| + 1e-3 RMS), and y unchanged bit for bit."""
+    import parity
+    w = _workload(name)
+    inp = synth.make_inputs(w)
+    di = sdev.upload(inp)
+    y0, out0 = parity.gpu_forward(w, di)
+    y1, out = forward_saving(w, di)
+    assert torch.equal(y0, y1)
+    ors = parity.OracleSide(inp)
+    N, k, I, S = w.N, w.k, w.I, w.S
+    off = out["offsets"].cpu().numpy()
+    tor = out["token_of_row"].cpu().numpy()
+    A = int(off[-1])
+    rows = np.concatenate([np.arange(A), N * k + np.arange(N * S)])
+    toks = np.concatenate([tor[:A], np.tile(np.arange(N), S)])
+    grp = np.concatenate([np.repeat(np.arange(w.E), np.diff(off)), w.E + np.repeat(np.arange(S), N)])
+    which = [("act_u", 1)] + ([("act_a", 0)] if w.activation == "swiglu" else [])
+    refs, gots = {}, {}
+    for name_, pos in which:
+        got = out[name_].float().cpu().numpy()[rows].astype(np.float64)
+        ref = np.zeros_like(got)
+        for gi in np.unique(grp):
+            sel = grp == gi
+            W = (ors.expert(int(gi)) if gi < w.E else ors.shared(int(gi - w.E)))[pos]
+            ref[sel] = ors.x[toks[sel]] @ W.T
+        refs[name_], gots[name_] = ref, got
+    clamped = np.zeros(refs["act_u"].shape, bool)
+    n_clamped = 0
+    if w.activation == "swiglu" and w.clip > 0:
+        # elements the forward clamps carry an infinite u whose sign times the
+        # sign of a is the sign of h; those within 1e-4 of the clip may go
+        # either way
+        a, u = refs["act_a"], refs["act_u"]
+        hpre = a / (1.0 + np.exp(-a)) * u
+        clamped = np.abs(hpre) > w.clip * (1 + 1e-4)
+        near = np.abs(np.abs(hpre) - w.clip) <= w.clip * 1e-4
+        gu = gots["act_u"]
+        assert np.all(np.isinf(gu[clamped]))
+        assert np.all(np.sign(gu[clamped]) * np.sign(a[clamped]) == np.sign(hpre[clamped]))
+        assert np.all(np.isfinite(gu[~clamped & ~near]))
+        n_clamped = int(clamped.sum())
+        clamped |= near
+    for name_, ref in refs.items():
+        got = gots[name_]
+        ok = ~clamped if name_ == "act_u" else np.ones(ref.shape, bool)
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        bad = np.abs(got[ok] - ref[ok]) > 2.0 ** -10 * np.abs(ref[ok]) + 1e-3 * rms
+        assert not bad.any(), (name_, int(bad.sum()))
+    _say(f"[saved] {name}: {A} routed rows + {N * S} shared rows match ({n_clamped} clamped)")
+    if name == "v41-clip-s":
+        assert n_clamped > 0.1 * clamped.size
 
 
 @pytest.mark.parametrize("gating", ["softmax", "sigmoid"])
@@ -269,6 +367,12 @@ def _oracle_token_grads(w, ors, route, disp, dy, toks):
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_backward_sampled(name):
+    # the capacity and DeepSeek-shaped layers run with the forward's saved
+    # pre-activations (what bench.py --backward times), the others recompute
+    _full_size_backward(name, saved=name in ("cap", "ds-P", "v41"))
+
+
+def _full_size_backward(name, saved):
     """The backward at the full workload sizes, in the configuration bench.py
     --backward times, checked on samples the oracle computes piece by piece:
     the weight gradients of a few experts restricted to a random subset of
@@ -284,9 +388,9 @@ def test_full_size_backward_sampled(name):
     _say(f"[bwd-full] {name}: generating inputs")
     inp = synth.make_inputs(w)
     di = sdev.upload(inp)
-    y, out = parity.gpu_forward(w, di)
+    y, out = forward_saving(w, di) if saved else parity.gpu_forward(w, di)
     del y
-    g = parity.to_np(out)
+    g = parity.to_np({n: v for n, v in out.items() if n not in ("act_a", "act_u")})
     ors = parity.OracleSide(inp)
     route = ors.route()
     N, d, E, k, I, S = w.N, w.d, w.E, w.k, w.I, w.S
@@ -378,4 +482,4 @@ def test_full_size_backward_sampled(name):
     ref_lb = dz_all.sum(0).cpu().numpy()
     glb = t["d_logit_bias"].cpu().numpy().astype(np.float64)
     assert np.max(np.abs(glb - ref_lb)) <= 1e-5 * max(np.max(np.abs(ref_lb)), 1e-30) + 1e-6
-    _say(f"[bwd-full] {name}: {rep}")
+    _say(f"[bwd-full] {name} (saved activations: {saved}): {rep}")

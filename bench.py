@@ -170,6 +170,23 @@ def cpu_baseline_backward(w, inp, budget_s=15.0):
             "host_cpu_count": len(os.sched_getaffinity(0))}
 
 
+def roofline_entry(flops, nbytes, ms, traffic):
+    """The roofline entry of a launch with the given algorithmic flops and
+    bytes: bound by HBM when its flops per byte are below the ridge (peak
+    flops / peak bandwidth, 312.5 flop/B), else by the matrix cores."""
+    ridge = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    intensity = flops / max(nbytes, 1)
+    if intensity < ridge:
+        ach = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "traffic": traffic, "algorithmic_per_launch": nbytes,
+                "flop_per_byte": intensity}
+    ach = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_MFMA_TFLOPS, "traffic": traffic, "algorithmic_per_launch": flops,
+            "flop_per_byte": intensity}
+
+
 def pmc_traffic(kernel: str, workload: str, src_hash: str):
     """HBM traffic of one launch from a committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
@@ -294,24 +311,15 @@ def main():
     tokens_s = w.N / (ms_step * 1e-3)
     layer_tflops = flops / (ms_step * 1e-3) / 1e12
     layer_gbs = nbytes / (ms_step * 1e-3) / 1e9
-    decode = w.N <= 64
     src = open(os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc", "gemm.hip"), "rb").read()
     src_hash = hashlib.sha256(src).hexdigest()
     # the gate/up grouped GEMM (ffn_gemm_dl<GATEUP, 256, 64, 2> for prefill,
     # ffn_gemm_bf16<GATEUP, 32, ...> for decode batches)
     kname = "ffn_gemm_gate_up"
     traffic = pmc_traffic(kname, w.name, src_hash)
-    if decode:
-        ach = gu_bytes / (gu_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": ach / PEAK_HBM_GBS, "traffic": traffic}
-    else:
-        ach = gu_flops / (gu_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_MFMA_TFLOPS, "traffic": traffic}
+    roof = roofline_entry(gu_flops, gu_bytes, gu_ms, traffic)
     roof["kernel"] = kname
     roof["ms_per_launch"] = gu_ms
-    roof["algorithmic_per_launch"] = gu_bytes if decode else gu_flops
 
     if args.calibrate_copy:
         a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
@@ -456,17 +464,24 @@ def bench_backward(args, w, inp, di, p):
     # recomputation of a and u (m-1 products) is counted apart.
     flops = (1 + m + (m - 1)) * 2 * d * I * rows + 4 * N * d * E
     flops_recompute = (m - 1) * 2 * d * I * rows
-    wg_flops = m * 2 * d * I * rows          # the weight-gradient stage: m launches
-    per_launch = wg_flops / m
-    ach = per_launch / (wg_ms / m * 1e-3) / 1e12
+    # the weight-gradient stage: m launches of 2·d·I flop per row; each writes
+    # every expert's and shared expert's float32 dW and reads its two operands
+    # (bf16 rows) once
+    per_launch = 2 * d * I * rows
+    per_launch_bytes = (E + S) * d * I * 4 + rows * (d + I) * 2
     src = open(os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc", "backward.hip"),
                "rb").read()
     kname = "bwd_gemm_wgrad"
-    roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-            "frac": ach / PEAK_MFMA_TFLOPS,
-            "traffic": pmc_traffic(kname, w.name, hashlib.sha256(src).hexdigest()),
-            "kernel": kname, "launches_per_step": m, "ms_per_launch": wg_ms / m,
-            "algorithmic_per_launch": per_launch}
+    roof = roofline_entry(per_launch, per_launch_bytes, wg_ms / m,
+                          pmc_traffic(kname, w.name, hashlib.sha256(src).hexdigest()))
+    roof.update({"kernel": kname, "launches_per_step": m, "ms_per_launch": wg_ms / m})
+    if args.calibrate_copy:
+        a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy of 256 MiB done")
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the float64 CPU oracle's backward on a bounded sample ...")

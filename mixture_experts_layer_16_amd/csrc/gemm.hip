@@ -1077,6 +1077,7 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
     MOE_DL(128, 64, 2, 4)
     MOE_DL(256, 64, 2, 8)
     MOE_DL(256, 32, 3, 8)
+    MOE_DL(128, 64, 3, 4)
     return hipErrorInvalidValue;
 #undef MOE_DL
   } else if (dtype == MOE_BF16) {
@@ -1128,7 +1129,11 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   // second launch needs enough remainder tiles to fill the chip (measured:
   // -3% time with 257 or 385 groups, +8% with 65).
   const bool split = cfg_up.dl && bm == 256 && cfg_dn.dl && cfg_dn.bm == 256 && G >= 128;
-  const GemmCfg cfg_s{128, 256, 64, 2, 2, 1, 2, 0, 1};
+  // remainder tiles: 4 waves; three stages in the gate/up pass (its copies need
+  // the deeper prefetch: -4% time for the stage on ds-P and v41), two in the
+  // down pass (three measured +3%)
+  const GemmCfg cfg_s{128, 256, 64, 2, 2, 1, 3, 0, 1};
+  const GemmCfg cfg_s_dn{128, 256, 64, 2, 2, 1, 2, 0, 1};
   int32_t* plan_s = split ? c.plan + plan_stride(G) : nullptr;
   const int64_t mt = max_mtiles(c, bm);
   const int64_t mt_s = split ? (int64_t)G : 0;
@@ -1199,7 +1204,7 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   if (err == hipSuccess && split) {
     GemmParams ds = dn;
     ds.plan = plan_s;
-    err = launch_gemm<MODE_DOWN>(ds, c.dtype, cfg_s, mt_s, s);
+    err = launch_gemm<MODE_DOWN>(ds, c.dtype, cfg_s_dn, mt_s, s);
   }
   mark(5);
   return err;

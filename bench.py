@@ -213,6 +213,8 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (moe_backward on the forward's routing and "
                          "saved pre-activations) instead of the forward")
+    ap.add_argument("--dw-bf16", action="store_true",
+                    help="with --backward: weight gradients written as bf16 instead of float32")
     ap.add_argument("--recompute", action="store_true",
                     help="with --backward: the forward saves no pre-activations, the backward "
                          "recomputes them")
@@ -395,24 +397,25 @@ def bench_backward(args, w, inp, di, p):
     L.moe_forward(p, wts, di.x, di.logit_bias, di.sel_bias, di.modality, y, rt, ws)
     torch.cuda.synchronize()
     del ws, y
+    wt = torch.bfloat16 if args.dw_bf16 else f32
     g = dict(dx=torch.empty((N, d), dtype=f32, device=dev),
-             dw_router=torch.empty((E, d), dtype=f32, device=dev),
-             dw_up=torch.empty((E, I, d), dtype=f32, device=dev),
-             dw_down=torch.empty((E, d, I), dtype=f32, device=dev),
+             dw_router=torch.empty((E, d), dtype=wt, device=dev),
+             dw_up=torch.empty((E, I, d), dtype=wt, device=dev),
+             dw_down=torch.empty((E, d, I), dtype=wt, device=dev),
              d_logit_bias=torch.empty(E, dtype=f32, device=dev))
     if swiglu:
-        g["dw_gate"] = torch.empty((E, I, d), dtype=f32, device=dev)
+        g["dw_gate"] = torch.empty((E, I, d), dtype=wt, device=dev)
     if S:
-        g["dws_up"] = torch.empty((S, I, d), dtype=f32, device=dev)
-        g["dws_down"] = torch.empty((S, d, I), dtype=f32, device=dev)
+        g["dws_up"] = torch.empty((S, I, d), dtype=wt, device=dev)
+        g["dws_down"] = torch.empty((S, d, I), dtype=wt, device=dev)
         if swiglu:
-            g["dws_gate"] = torch.empty((S, I, d), dtype=f32, device=dev)
+            g["dws_gate"] = torch.empty((S, I, d), dtype=wt, device=dev)
     dy = torch.from_numpy(synth.upstream_grad(w)).to(dev)
     bws = L.backward_workspace(p)
-    gr = L.grads(**g)
+    gr = L.grads(dw_bf16=args.dw_bf16, **g)
     stream = torch.cuda.current_stream()
     log(f"backward: workspace {bws.numel() / 2**30:.2f} GiB, gradients "
-        f"{sum(t.numel() for t in g.values()) * 4 / 2**30:.2f} GiB")
+        f"{sum(t.numel() * t.element_size() for t in g.values()) / 2**30:.2f} GiB")
 
     def step(prof=None):
         L.moe_backward_ex(p, wts, di.x, rt, dy, gr, prof, bws, stream=stream)
@@ -468,7 +471,7 @@ def bench_backward(args, w, inp, di, p):
     # every expert's and shared expert's float32 dW and reads its two operands
     # (bf16 rows) once
     per_launch = 2 * d * I * rows
-    per_launch_bytes = (E + S) * d * I * 4 + rows * (d + I) * 2
+    per_launch_bytes = (E + S) * d * I * (2 if args.dw_bf16 else 4) + rows * (d + I) * 2
     src = open(os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc", "backward.hip"),
                "rb").read()
     kname = "bwd_gemm_wgrad"
@@ -502,6 +505,7 @@ def bench_backward(args, w, inp, di, p):
         "data": "synthetic (seeded; random-init weights of the stated shapes; dy ~ N(0, 1))",
         "config": {"workload": w.name, "pass": "backward",
                    "activations": "recomputed" if args.recompute else "saved by the forward",
+                   "weight_gradients": "bf16" if args.dw_bf16 else "float32",
                    "N": N, "d": d, "E": E, "S": S,
                    "k": k, "I": I, "capacity_factor": w.f, "gating": w.gating,
                    "activation": w.activation, "kept_assignments": A},

@@ -310,20 +310,24 @@ int moe_balance(const moe_problem* p, const double* logits, const int32_t* count
                 double* aux, float* sel_bias, float gamma, void* ws, size_t ws_bytes,
                 void* stream);
 
-/* Gradients written by moe_backward (device pointers, float32, same layouts
- * as the weights they belong to). */
+/* Gradients written by moe_backward (device pointers, same layouts as the
+ * weights they belong to).  Weight gradients (dw_*, dws_*) are float32, or
+ * bf16 (raw 16-bit words, round to nearest even) when dw_bf16 = 1; dx, the
+ * logit-offset gradient, dz and dg are float32. */
 typedef struct {
   float* dx;            /* [N][d] required */
-  float* dw_router;     /* [E][d] required */
-  float* dw_gate;       /* [E][I][d] required for MOE_SWIGLU, unused for MOE_RELU */
-  float* dw_up;         /* [E][I][d] required */
-  float* dw_down;       /* [E][d][I] required */
-  float* dws_gate;      /* [S][I][d] required when S > 0 and MOE_SWIGLU */
-  float* dws_up;        /* [S][I][d] required when S > 0 */
-  float* dws_down;      /* [S][d][I] required when S > 0 */
+  void* dw_router;      /* [E][d] required */
+  void* dw_gate;        /* [E][I][d] required for MOE_SWIGLU, unused for MOE_RELU */
+  void* dw_up;          /* [E][I][d] required */
+  void* dw_down;        /* [E][d][I] required */
+  void* dws_gate;       /* [S][I][d] required when S > 0 and MOE_SWIGLU */
+  void* dws_up;         /* [S][I][d] required when S > 0 */
+  void* dws_down;       /* [S][d][I] required when S > 0 */
   float* d_logit_bias;  /* [E] nullable: gradient of the logit offset o (= sum_t dz_t) */
   float* dz;            /* [N][E] nullable: gradient of the logits */
   float* dg;            /* [N*k] nullable: gradient of the gate weights (0 for dropped slots) */
+  int32_t dw_bf16;      /* 0: weight gradients float32; 1: bf16 (half the bytes written,
+                           which bound the weight-gradient products of small experts) */
 } moe_grads;
 
 /* Bytes of device workspace moe_backward needs for problem p (host). */

@@ -62,7 +62,7 @@ class Routing(ctypes.Structure):
 class Grads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up",
-                 "dws_down", "d_logit_bias", "dz", "dg")]
+                 "dws_down", "d_logit_bias", "dz", "dg")] + [("dw_bf16", ctypes.c_int32)]
 
 
 class Profile(ctypes.Structure):
@@ -300,8 +300,8 @@ def moe_backward_ex(p, w: "Weights", x, routing_in: "Routing", dy, grads_out: "G
     _check("moe_backward_ex", st)
 
 
-def grads(**tensors) -> Grads:
-    return Grads(**{k: ptr(v) for k, v in tensors.items()})
+def grads(dw_bf16=False, **tensors) -> Grads:
+    return Grads(**{k: ptr(v) for k, v in tensors.items()}, dw_bf16=int(dw_bf16))
 
 
 def weights(w_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None) -> Weights:

@@ -545,6 +545,7 @@ int moe_backward_ex(const moe_problem* p, const moe_weights* w, const void* x,
   if (!g.dx || !g.dw_router || !g.dw_up || !g.dw_down || (swiglu && !g.dw_gate))
     return MOE_ERR_NULL;
   if (shared && (!g.dws_up || !g.dws_down || (swiglu && !g.dws_gate))) return MOE_ERR_NULL;
+  if (g.dw_bf16 != 0 && g.dw_bf16 != 1) return MOE_ERR_INVALID;
   {
     const void* ptrs[] = {x,          w->w_router, w->w_gate,  w->w_up,   w->w_down,
                           w->ws_gate, w->ws_up,    w->ws_down, dy,        g.dx,
@@ -585,6 +586,7 @@ int moe_backward_ex(const moe_problem* p, const moe_weights* w, const void* x,
   c.dw_router = g.dw_router;
   c.dw_gate = g.dw_gate; c.dw_up = g.dw_up; c.dw_down = g.dw_down;
   c.dws_gate = g.dws_gate; c.dws_up = g.dws_up; c.dws_down = g.dws_down;
+  c.dw_bf16 = g.dw_bf16;
   c.d_logit_bias = g.d_logit_bias;
   c.dz_out = g.dz;
   c.dg_out = g.dg;

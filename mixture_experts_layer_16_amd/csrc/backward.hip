@@ -49,8 +49,9 @@ struct Operand {
 struct BwdGemmParams {
   Operand A, B, A2, B2;      // A2/B2: optional second product into the same C
   int two;                   // use A2/B2
-  float* C;                  // row mode: [rows][ldc]; weight mode: routed groups' matrices
-  float* Cs;                 // weight mode: dense groups' matrices
+  void* C;                   // row mode: float [rows][ldc]; weight mode: routed groups' matrices
+  void* Cs;                  // weight mode: dense groups' matrices
+  int out_bf16;              // weight mode: C / Cs are bf16 (partials stay float)
   int64_t ldc, c_gstride;
   int M, N, K, K2;           // extents (row mode: M from the plan; weight mode: K from it)
   int mode;                  // 0: tiles over the plan's rows; 1: K = a group's rows
@@ -131,7 +132,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) 
   // ---- tile decode
   int g, m0, n0, Mlim, Klim;
   int64_t rb;
-  float* Cg = p.C;   // weight mode: this tile's output matrix
+  char* Cg = static_cast<char*>(p.C);   // this tile's output matrix (bytes)
+  bool obf = false;                      // ... holds bf16 (else float)
   const int ntn = (p.N + BN - 1) / BN;
   if (p.mode == 0) {
     const int32_t* tile_start = p.plan;
@@ -188,23 +190,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) 
       g = gv;
       rb = p.plan[p.G + 1 + g];
       Klim = p.plan[p.G + 1 + p.G + g];
-      Cg = p.C + g * p.c_gstride;
+      obf = p.out_bf16;
+      Cg = static_cast<char*>(p.C) + g * p.c_gstride * (obf ? 2 : 4);
     } else {
       const int sd = (gv - p.n_gather) / p.pieces, q = (gv - p.n_gather) % p.pieces;
       g = p.n_gather + sd;
       rb = p.plan[p.G + 1 + g] + (int64_t)q * p.kchunk;
       Klim = p.plan[p.G + 1 + p.G + g];
       if (p.pieces > 1) Klim = min(p.kchunk, Klim - q * p.kchunk);
-      Cg = p.pieces == 1 ? p.Cs + (int64_t)sd * p.c_gstride
-                         : p.Cpart + (int64_t)(sd * p.pieces + q) * p.c_gstride;
+      obf = p.out_bf16 && p.pieces == 1;
+      Cg = p.pieces == 1
+               ? static_cast<char*>(p.Cs) + (int64_t)sd * p.c_gstride * (obf ? 2 : 4)
+               : reinterpret_cast<char*>(p.Cpart + (int64_t)(sd * p.pieces + q) * p.c_gstride);
     }
     Mlim = p.M;
     if (Klim <= 0) {
       // no rows: the gradient of this group's weights (or piece) is zero
       for (int i = tid; i < BM * BN / 4; i += 64 * NW) {
         const int m = m0 + i / (BN / 4), n = n0 + 4 * (i % (BN / 4));
-        if (m < p.M && n < p.N)
-          *reinterpret_cast<float4*>(Cg + (int64_t)m * p.ldc + n) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (m < p.M && n < p.N) {
+          if (obf)
+            *reinterpret_cast<uint2*>(Cg + ((int64_t)m * p.ldc + n) * 2) = make_uint2(0u, 0u);
+          else
+            *reinterpret_cast<float4*>(Cg + ((int64_t)m * p.ldc + n) * 4) =
+                make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
       return;
     }
@@ -426,7 +436,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) 
   // ---- store: acc[i][j] is the 32 x 32 block of C^T; element v of lane
   // (lr, lh) is row 32 i + lr and column 8 (v / 4) + 4 lh + v % 4 of fragment j,
   // so each lane holds runs of 4 consecutive columns
-  float* C = Cg;
   {
     // through LDS (free: run() ended with a barrier after its last reads), one
     // 32-column fragment per pass, so each global store instruction writes
@@ -454,10 +463,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_gemm_dl(BwdGemmParams p) 
         const int n = n0 + wn * WCOLS + 32 * j + 4 * c4;
         // non-temporal: the results are not read again by this kernel
         // (measured: about 1% less time for the backward)
-        if (m < Mlim && n < p.N)
-          __builtin_nontemporal_store(
-              f32x4_t{v.x, v.y, v.z, v.w},
-              reinterpret_cast<f32x4_t*>(C + (p.mode == 0 ? rb + m : (int64_t)m) * p.ldc + n));
+        if (m < Mlim && n < p.N) {
+          const int64_t e = (p.mode == 0 ? rb + m : (int64_t)m) * p.ldc + n;
+          if (obf) {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t b = {f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                               f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+            __builtin_nontemporal_store(b, reinterpret_cast<u32x2_t*>(Cg + e * 2));
+          } else {
+            __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w},
+                                        reinterpret_cast<f32x4_t*>(Cg + e * 4));
+          }
+        }
       }
     }
   }
@@ -754,10 +771,10 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict
 }
 
 // out[s][i] = sum over q (in order) of part[s][q][i]; n (a multiple of 4)
-// elements per matrix, P pieces, blockIdx.y = s
+// elements per matrix, P pieces, blockIdx.y = s; out float or (BF16) bf16
+template <bool BF16>
 __global__ __launch_bounds__(256) void reduce_pieces_kernel(const float* __restrict__ part,
-                                                            int P, int64_t n,
-                                                            float* __restrict__ out,
+                                                            int P, int64_t n, void* out,
                                                             int64_t out_stride) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
@@ -767,7 +784,13 @@ __global__ __launch_bounds__(256) void reduce_pieces_kernel(const float* __restr
     const float4 b = *reinterpret_cast<const float4*>(src + (int64_t)q * n);
     a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
   }
-  *reinterpret_cast<float4*>(out + (int64_t)blockIdx.y * out_stride + i) = a;
+  const int64_t o = (int64_t)blockIdx.y * out_stride + i;
+  if (BF16)
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) =
+        make_uint2(f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16),
+                   f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16));
+  else
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = a;
 }
 
 inline unsigned blocks_of(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
@@ -979,12 +1002,18 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
     hipError_t e = launch_bwd_gemm<1, 1, cfg[0], cfg[1], cfg[2], cfg[3]>(pp, tiles, s);
     if (e != hipSuccess || pp.pieces == 1 || pp.G == pp.n_gather) return e;
     const int64_t n = (int64_t)M * Nn;
-    reduce_pieces_kernel<<<dim3(blocks_of(n / 4, 256), (unsigned)(pp.G - pp.n_gather)), 256, 0,
-                           s>>>(pp.Cpart, pp.pieces, n, pp.Cs, pp.c_gstride);
+    const dim3 grid(blocks_of(n / 4, 256), (unsigned)(pp.G - pp.n_gather));
+    if (pp.out_bf16)
+      reduce_pieces_kernel<true><<<grid, 256, 0, s>>>(pp.Cpart, pp.pieces, n, pp.Cs,
+                                                      pp.c_gstride);
+    else
+      reduce_pieces_kernel<false><<<grid, 256, 0, s>>>(pp.Cpart, pp.pieces, n, pp.Cs,
+                                                       pp.c_gstride);
     return hipGetLastError();
   };
   // dW_down[e] = sum_r dy_t^T (g h_r)   ([d][I])
   q.M = d; q.N = I; q.ldc = I; q.c_gstride = (int64_t)d * I;
+  q.out_bf16 = c.dw_bf16;
   q.A = dyin; q.B = hgin; q.C = c.dw_down; q.Cs = c.dws_down;
   MOE_CHK(wgemm(q, d, I));
   // dW_gate[e] = sum_r da_r^T x_t, dW_up[e] = sum_r du_r^T x_t   ([I][d])
@@ -1003,6 +1032,7 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   q.mode = 0;
   q.N = d; q.ldc = d; q.K = I; q.K2 = I;
   q.C = dxp; q.Cs = nullptr;
+  q.out_bf16 = 0;
   if (swiglu) {
     q.A = dain;
     q.B = Wop(c.wg, c.sg, d);
@@ -1046,6 +1076,7 @@ hipError_t launch_backward(const BwdCall& c, hipStream_t s) {
   qr.B = Operand{x, x, 0, d, 0};
   qr.C = c.dw_router;
   qr.Cs = c.dw_router;
+  qr.out_bf16 = c.dw_bf16;
   qr.c_gstride = (int64_t)E * d;
   qr.pieces = pieces_of(N, kRouterChunk);
   qr.kchunk = chunk_of(N, kRouterChunk);

@@ -177,7 +177,9 @@ struct BwdCall {
   const int32_t *topk_idx, *offsets, *row_of, *token_of_row;
   const float* topk_w;
   const uint16_t *act_a, *act_u;               // optional fp16 saved pre-activations
-  float *dx, *dw_router, *dw_gate, *dw_up, *dw_down, *dws_gate, *dws_up, *dws_down;
+  float* dx;
+  void *dw_router, *dw_gate, *dw_up, *dw_down, *dws_gate, *dws_up, *dws_down;
+  int dw_bf16;                                 // weight gradients in bf16
   float *d_logit_bias, *dz_out, *dg_out;       // nullable
   void* ws;
   BwdLayout L;

@@ -304,8 +304,20 @@ def test_backward_workspace_grows_with_tokens(L):
 
 
 def test_grads_struct_matches_the_header_layout(L):
-    assert ctypes.sizeof(L.Grads) == 11 * 8
-    assert L.Grads.dg.offset == 80
+    assert ctypes.sizeof(L.Grads) == 12 * 8
+    assert L.Grads.dg.offset == 80 and L.Grads.dw_bf16.offset == 88
+
+
+def test_backward_rejects_a_bad_gradient_dtype(L):
+    fake = 0x10000
+    B = ctypes.byref
+    p = L.problem(64, 128, 8, 2, 64, S=1)
+    w = L.Weights(fake, fake, fake, fake, fake, fake, fake)
+    r = L.Routing(topk_idx=fake, topk_w=fake, logits=fake, offsets=fake, row_of=fake,
+                  token_of_row=fake)
+    g = L.Grads(dx=fake, dw_router=fake, dw_gate=fake, dw_up=fake, dw_down=fake, dws_gate=fake,
+                dws_up=fake, dws_down=fake, dw_bf16=2)
+    assert L.LIB.moe_backward(B(p), B(w), fake, B(r), fake, B(g), fake, 1 << 40, None) == -2
 
 
 def test_saved_activation_pointers_are_validated(L):

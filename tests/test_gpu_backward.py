@@ -35,6 +35,11 @@ pytestmark = pytest.mark.gpu
 RMS_TOL = 4e-3
 GROUP_RMS_TOL = 6e-3
 MAX_TOL = 0.25
+# bf16 weight gradients (dw_bf16): a third rounding (the result's, relative
+# error <= u) on top of the two operands': RMS about sqrt(3/3) u = 3.9e-3 of
+# the result's RMS at most
+BF16_RMS_TOL = 5e-3
+BF16_GROUP_RMS_TOL = 7e-3
 
 
 def _say(*a):
@@ -71,9 +76,9 @@ def _stack(lst, shape):
     return np.stack([np.zeros(shape) if a is None else a for a in lst]) if lst else None
 
 
-def gpu_backward(w, di, out, dy):
+def gpu_backward(w, di, out, dy, dw_bf16=False):
     """moe_backward on the routing arrays of a moe_forward call; returns numpy
-    gradients."""
+    gradients (weight gradients as float32 numbers also when bf16)."""
     from mixture_experts_layer_16_amd import _lib as L
     import parity
     p = parity.problem_of(w)
@@ -84,24 +89,28 @@ def gpu_backward(w, di, out, dy):
     def buf(*shape):
         return torch.full(shape, np.nan, dtype=f32, device=dev)
 
+    def wbuf(*shape):
+        return torch.full(shape, np.nan, dtype=torch.bfloat16 if dw_bf16 else f32, device=dev)
+
     swiglu = w.activation == "swiglu"
-    t = dict(dx=buf(max(1, N), d), dw_router=buf(E, d), dw_up=buf(E, I, d), dw_down=buf(E, d, I),
-             d_logit_bias=buf(E), dz=buf(max(1, N * E)), dg=buf(max(1, N * k)))
+    t = dict(dx=buf(max(1, N), d), dw_router=wbuf(E, d), dw_up=wbuf(E, I, d),
+             dw_down=wbuf(E, d, I), d_logit_bias=buf(E), dz=buf(max(1, N * E)),
+             dg=buf(max(1, N * k)))
     if swiglu:
-        t["dw_gate"] = buf(E, I, d)
+        t["dw_gate"] = wbuf(E, I, d)
     if S:
-        t["dws_up"] = buf(S, I, d)
-        t["dws_down"] = buf(S, d, I)
+        t["dws_up"] = wbuf(S, I, d)
+        t["dws_down"] = wbuf(S, d, I)
         if swiglu:
-            t["dws_gate"] = buf(S, I, d)
+            t["dws_gate"] = wbuf(S, I, d)
     dyt = torch.from_numpy(np.ascontiguousarray(dy, np.float32)).to(dev)
     wts = L.weights(di.w_router, di.w_gate, di.w_up, di.w_down, di.ws_gate, di.ws_up,
                     di.ws_down)
     rt = L.routing(**{n: v for n, v in out.items() if v is not None})
     ws = L.backward_workspace(p)
-    L.moe_backward(p, wts, di.x, rt, dyt, L.grads(**t), ws)
+    L.moe_backward(p, wts, di.x, rt, dyt, L.grads(dw_bf16=dw_bf16, **t), ws)
     torch.cuda.synchronize()
-    res = {n: v.cpu().numpy() for n, v in t.items()}
+    res = {n: v.float().cpu().numpy() for n, v in t.items()}
     return res, (p, wts, rt, dyt, t, ws)
 
 
@@ -132,7 +141,7 @@ def forward_saving(w, di):
     return y, out
 
 
-def check_backward(w, inp=None, saved=False):
+def check_backward(w, inp=None, saved=False, dw_bf16=False):
     import parity
     inp = inp or synth.make_inputs(w)
     di = sdev.upload(inp)
@@ -144,7 +153,7 @@ def check_backward(w, inp=None, saved=False):
     assert np.array_equal(gidx, ors.route()["idx"]), "near-tie routing: pick another seed"
     parity.check_dispatch(ors, g, gidx, rep)
     dy = synth.upstream_grad(w)
-    gb, _ = gpu_backward(w, di, out, dy)
+    gb, _ = gpu_backward(w, di, out, dy, dw_bf16)
     ref = oracle_backward(w, ors, dy)
     N, d, E, k, I, S = w.N, w.d, w.E, w.k, w.I, w.S
     swiglu = w.activation == "swiglu"
@@ -182,9 +191,14 @@ def check_backward(w, inp=None, saved=False):
     rep["dropped"] = int(dropped.sum())
     rep["empty_experts"] = int((rows_per_e == 0).sum())
     rep["saved"] = saved
+    rep["dw_bf16"] = dw_bf16
     _say(f"[backward] {w.name} {rep}")
+    def tols(n):
+        if dw_bf16 and n.startswith("dw"):
+            return BF16_RMS_TOL, BF16_GROUP_RMS_TOL
+        return RMS_TOL, GROUP_RMS_TOL
     bad = {n: v for n, v in errs.items()
-           if not (v[0] <= RMS_TOL and v[1] <= MAX_TOL and v[2] <= GROUP_RMS_TOL)}
+           if not (v[0] <= tols(n)[0] and v[1] <= MAX_TOL and v[2] <= tols(n)[1])}
     assert not bad, (bad, rep)
     return rep
 
@@ -209,6 +223,13 @@ def _workload(name):
     if name == "v41-clip-s":
         return synth.derive(synth.get("v41-s"), name=name, clip=0.06)
     return synth.get(name)
+
+
+@pytest.mark.parametrize("name", ["cap-s", "ds-s", "v41-s", "relu-bf16-s", "mixd-s"])
+def test_backward_bf16_weight_gradients(name):
+    """dw_bf16 = 1: the weight gradients are written as bf16 (rounded once from
+    the same float32 results); empty experts' stay exactly zero."""
+    check_backward(synth.get(name), saved=name != "mixd-s", dw_bf16=True)
 
 
 @pytest.mark.parametrize("saved", [False, True])
@@ -372,7 +393,11 @@ def test_full_size_backward_sampled(name):
     _full_size_backward(name, saved=name in ("cap", "ds-P", "v41"))
 
 
-def _full_size_backward(name, saved):
+def test_full_size_backward_bf16_weight_gradients():
+    _full_size_backward("ds-P", saved=True, dw_bf16=True)
+
+
+def _full_size_backward(name, saved, dw_bf16=False):
     """The backward at the full workload sizes, in the configuration bench.py
     --backward times, checked on samples the oracle computes piece by piece:
     the weight gradients of a few experts restricted to a random subset of
@@ -403,26 +428,28 @@ def _full_size_backward(name, saved):
     dev = di.x.device
     f32 = torch.float32
     swiglu = w.activation == "swiglu"
+    wt = torch.bfloat16 if dw_bf16 else f32
     t = dict(dx=torch.empty((N, d), dtype=f32, device=dev),
-             dw_router=torch.empty((E, d), dtype=f32, device=dev),
-             dw_up=torch.empty((E, I, d), dtype=f32, device=dev),
-             dw_down=torch.empty((E, d, I), dtype=f32, device=dev),
+             dw_router=torch.empty((E, d), dtype=wt, device=dev),
+             dw_up=torch.empty((E, I, d), dtype=wt, device=dev),
+             dw_down=torch.empty((E, d, I), dtype=wt, device=dev),
              d_logit_bias=torch.empty(E, dtype=f32, device=dev),
              dz=torch.empty(N * E, dtype=f32, device=dev),
              dg=torch.empty(N * k, dtype=f32, device=dev))
     if swiglu:
-        t["dw_gate"] = torch.empty((E, I, d), dtype=f32, device=dev)
+        t["dw_gate"] = torch.empty((E, I, d), dtype=wt, device=dev)
     if S:
-        t["dws_up"] = torch.empty((S, I, d), dtype=f32, device=dev)
-        t["dws_down"] = torch.empty((S, d, I), dtype=f32, device=dev)
+        t["dws_up"] = torch.empty((S, I, d), dtype=wt, device=dev)
+        t["dws_down"] = torch.empty((S, d, I), dtype=wt, device=dev)
         if swiglu:
-            t["dws_gate"] = torch.empty((S, I, d), dtype=f32, device=dev)
+            t["dws_gate"] = torch.empty((S, I, d), dtype=wt, device=dev)
     wts = L.weights(di.w_router, di.w_gate, di.w_up, di.w_down, di.ws_gate, di.ws_up,
                     di.ws_down)
     rt = L.routing(**{n: v for n, v in out.items() if v is not None})
     dyt = torch.from_numpy(dy).to(dev)
-    L.moe_backward(parity.problem_of(w), wts, di.x, rt, dyt, L.grads(**t),
+    L.moe_backward(parity.problem_of(w), wts, di.x, rt, dyt, L.grads(dw_bf16=dw_bf16, **t),
                    L.backward_workspace(parity.problem_of(w)))
+    wtol = BF16_RMS_TOL if dw_bf16 else RMS_TOL
     torch.cuda.synchronize()
     rng = np.random.default_rng(99)
     rep = {}
@@ -450,17 +477,17 @@ def _full_size_backward(name, saved):
         wgU = None if wg is None else wg[U]
         _, rg, ru, rd = O.expert_ffn_backward(ors.x[toks], wgU, wu[U], wd[:, U], w.activation,
                                               w.clip, d_out)
-        got = {"up": t[pre + "up"][ei].index_select(0, Ut).cpu().numpy(),
-               "down": t[pre + "down"][ei].index_select(1, Ut).cpu().numpy()}
+        got = {"up": t[pre + "up"][ei].index_select(0, Ut).float().cpu().numpy(),
+               "down": t[pre + "down"][ei].index_select(1, Ut).float().cpu().numpy()}
         ref = {"up": ru, "down": rd}
         if swiglu:
-            got["gate"] = t[pre + "gate"][ei].index_select(0, Ut).cpu().numpy()
+            got["gate"] = t[pre + "gate"][ei].index_select(0, Ut).float().cpu().numpy()
             ref["gate"] = rg
         for n_ in got:
             r_, mx, _ = _rel(got[n_], ref[n_])
             rep[f"{pre}{n_}[{ei}]"] = round(r_, 5)
             worst = max(worst, r_)
-            assert r_ <= RMS_TOL and mx <= MAX_TOL, (name, e, n_, r_, mx)
+            assert r_ <= wtol and mx <= MAX_TOL, (name, e, n_, r_, mx)
     # -- dx, dg, dz of sampled tokens
     toks = np.unique(np.linspace(0, N - 1, min(N, 12)).astype(np.int64))
     Tt = torch.from_numpy(toks).to(dev)
@@ -476,10 +503,10 @@ def _full_size_backward(name, saved):
     dz_all = t["dz"].view(N, E).double()
     x64 = torch.from_numpy(ors.x).to(dev)
     ref_wr = (dz_all.t() @ x64).cpu().numpy()
-    r_, mx, _ = _rel(t["dw_router"].cpu().numpy(), ref_wr)
+    r_, mx, _ = _rel(t["dw_router"].float().cpu().numpy(), ref_wr)
     rep["dw_router_vs_own_dz"] = round(r_, 5)
-    assert r_ <= RMS_TOL and mx <= MAX_TOL
+    assert r_ <= wtol and mx <= MAX_TOL
     ref_lb = dz_all.sum(0).cpu().numpy()
     glb = t["d_logit_bias"].cpu().numpy().astype(np.float64)
     assert np.max(np.abs(glb - ref_lb)) <= 1e-5 * max(np.max(np.abs(ref_lb)), 1e-30) + 1e-6
-    _say(f"[bwd-full] {name} (saved activations: {saved}): {rep}")
+    _say(f"[bwd-full] {name} (saved activations: {saved}, bf16 dW: {dw_bf16}): {rep}")

@@ -20,6 +20,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
 constexpr int kXcds = 8;              // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kCus = 256;             // MI355X: compute units (32 per die)
 constexpr int kMaxRouterSplits = 32;  // split-K pieces of the router for small batches
 constexpr int kBalTokens = 64;        // tokens per block of the balance-statistics kernel
 constexpr int kBalMaxBlocks = 512;    // blocks (and partial rows) of that kernel at most

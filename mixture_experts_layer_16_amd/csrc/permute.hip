@@ -14,10 +14,10 @@
 //               expert), keeps per-wave running counts in LDS, then turns them
 //               into block-local ranks and a per-block histogram (also split by
 //               modality);
-//   2. scan:    per expert (one wave each), an exclusive scan of the block
-//               histograms gives each block's base rank and the expert's demand;
-//               kept = min(demand, C); an exclusive scan over experts gives the
-//               offsets;
+//   2. scan:    per expert, an exclusive scan of the block histograms (in
+//               runs of blocks, one thread per run) gives each block's base
+//               rank and the expert's demand; kept = min(demand, C); an
+//               exclusive scan over experts gives the offsets;
 //   3. scatter: rank = block base + local rank; kept iff rank < C.
 #include "moe_internal.h"
 
@@ -95,56 +95,86 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(
   }
 }
 
-// One wave per expert: the block histograms are scanned 64 blocks at a time
-// with a wave prefix sum and a running carry.
+// Block-histogram scan, one block of 1024 threads.  Thread t works on expert
+// e = t % E and on the c-th (c = t / E) of tpe <= 1024 / E runs of consecutive
+// blocks, so neighbouring threads read neighbouring words of a block record.
+// Pass 1 sums each run; an expert's run sums are added up in run order (LDS)
+// for each run's starting rank; pass 2 walks the run again and writes each
+// block's base rank.  Loads go out in batches of 8 blocks.
+constexpr int SCAN_BATCH = 8;
+
 __global__ __launch_bounds__(1024) void perm_scan_kernel(
     int32_t* __restrict__ blk, int nblk, int32_t* __restrict__ counts,
     int32_t* __restrict__ mod_counts, int32_t* __restrict__ offsets, int E, int64_t C) {
   __shared__ int32_t kept[kMaxExperts];
   __shared__ int32_t tmp[1024];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  for (int e = wave; e < E; e += nwaves) {
-    int carry = 0, m0 = 0, m1 = 0;
-    for (int b0 = 0; b0 < nblk; b0 += 64) {
-      const int b = b0 + lane;
-      int32_t* rec = blk + (int64_t)b * 3 * E;
-      int v = 0, a0 = 0, a1 = 0;
-      if (b < nblk) {
-        v = rec[e];
-        a0 = rec[E + e];
-        a1 = rec[2 * E + e];
-      }
-      int incl = v;
+  __shared__ int32_t part[3][1024];
+  const int tid = threadIdx.x;
+  // runs per expert (E <= 1024): as many as the threads allow, but no shorter
+  // than one batch of blocks, so the run sums stay few
+  const int tpe = max(1, min(1024 / E, (nblk + SCAN_BATCH - 1) / SCAN_BATCH));
+  const int e = tid % E, c = tid / E;
+  const bool act = c < tpe;
+  const int L = (nblk + tpe - 1) / tpe;
+  const int b0 = act ? c * L : 0;
+  const int b1 = act ? min(nblk, b0 + L) : 0;
+  int v = 0, a0 = 0, a1 = 0;
+  for (int b = b0; b < b1; b += SCAN_BATCH) {
+    int x[SCAN_BATCH], y0[SCAN_BATCH], y1[SCAN_BATCH];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
+    for (int i = 0; i < SCAN_BATCH; ++i) {
+      x[i] = y0[i] = y1[i] = 0;
+      if (b + i < b1) {
+        const int32_t* rec = blk + (int64_t)(b + i) * 3 * E;
+        x[i] = rec[e];
+        y0[i] = rec[E + e];
+        y1[i] = rec[2 * E + e];
       }
-      if (b < nblk) rec[e] = carry + incl - v;
-      carry += __shfl(incl, 63);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        a0 += __shfl_xor(a0, off);
-        a1 += __shfl_xor(a1, off);
-      }
-      m0 += a0;
-      m1 += a1;
     }
-    if (lane == 0) {
-      counts[e] = carry;
+#pragma unroll
+    for (int i = 0; i < SCAN_BATCH; ++i) {
+      v += x[i];
+      a0 += y0[i];
+      a1 += y1[i];
+    }
+  }
+  part[0][tid] = v;
+  part[1][tid] = a0;
+  part[2][tid] = a1;
+  __syncthreads();
+  if (act) {
+    int run = 0;   // ranks held by the expert's earlier runs
+    for (int q = 0; q < c; ++q) run += part[0][q * E + e];
+    for (int b = b0; b < b1; b += SCAN_BATCH) {
+      int x[SCAN_BATCH];
+#pragma unroll
+      for (int i = 0; i < SCAN_BATCH; ++i)
+        x[i] = (b + i < b1) ? blk[(int64_t)(b + i) * 3 * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < SCAN_BATCH; ++i)
+        if (b + i < b1) {
+          blk[(int64_t)(b + i) * 3 * E + e] = run;
+          run += x[i];
+        }
+    }
+    if (c == tpe - 1) {   // the last run ends at the expert's demand
+      int m0 = 0, m1 = 0;
+      for (int q = 0; q < tpe; ++q) {
+        m0 += part[1][q * E + e];
+        m1 += part[2][q * E + e];
+      }
+      counts[e] = run;
       if (mod_counts) {
         mod_counts[e] = m0;
         mod_counts[E + e] = m1;
       }
-      kept[e] = (C < 0 || carry < C) ? carry : (int)C;
+      kept[e] = (C < 0 || run < C) ? run : (int)C;
     }
   }
   __syncthreads();
   const int total = block_exclusive_scan_1024(kept, E, tmp);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = kept[e];
-  if (threadIdx.x == 0) offsets[E] = total;
+  for (int e2 = tid; e2 < E; e2 += blockDim.x) offsets[e2] = kept[e2];
+  if (tid == 0) offsets[E] = total;
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(

@@ -28,17 +28,24 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 //
 // Block: 4 waves; tile 128 tokens x 64 experts; wave w owns 32 tokens (two
 // 16-row fragments, read straight from global memory) and the block's 64
-// experts, whose 64 x 32 k-slice is staged once per step in LDS (double
-// buffered) for all four waves.  The reduction dimension may be split over
-// gridDim.z blocks (small batches); each split writes float64 partials
-// [split][N][E] and the top-k kernel adds them in split order.
+// experts, whose 64 x 128 k-chunk is staged in LDS (double buffered) for all
+// four waves.  The loads of chunk c+1 (both operands) are in flight while
+// chunk c is multiplied, so each wave keeps 12 16-byte loads per lane
+// outstanding instead of waiting on every 32-wide step.  The reduction
+// dimension may be split over gridDim.z blocks (small batches); each split
+// writes float64 partials [split][N][E] and the top-k kernel adds them in
+// split order.  The float64 accumulators see the 32-product partials in k
+// order whatever the chunking, so the logits do not depend on it.
 constexpr int RT_TOK = 128;
 constexpr int RT_EXP = 64;
 
-__global__ __launch_bounds__(256) void router_bf16_kernel(
+// RT_STEPS: 32-wide k steps per staged chunk; MINB: blocks per CU the register
+// budget allows (two-step chunks need the registers of two blocks per CU)
+template <int RT_STEPS, int MINB>
+__global__ __launch_bounds__(256, MINB) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, double* __restrict__ zpart,
     int64_t N, int d, int E, int ksplit_len) {
-  __shared__ __attribute__((aligned(16))) uint16_t bs[2][RT_EXP * 32];
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][RT_STEPS][RT_EXP * 32];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -56,8 +63,9 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     if (arow >= N) arow = N - 1;
     ap[i] = x + arow * (int64_t)d + kq * 8;
   }
-  // B staging: thread -> (expert row tid / 4, chunk tid % 4); position of chunk
-  // c of row e in LDS: c ^ ((e >> 2) & 3), conflict-free for the 16-row reads
+  // B staging: thread -> (expert row tid / 4, chunk tid % 4) of each step; position
+  // of chunk c of row e in LDS: c ^ ((e >> 2) & 3), conflict-free for the
+  // 16-row reads
   const int se = tid >> 2, sc = tid & 3;
   int ge = e0 + se;
   if (ge >= E) ge = E - 1;
@@ -80,35 +88,60 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
 
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  auto ldb = [&](int k0) {
-    return (k0 + sc * 8 < k_hi) ? *reinterpret_cast<const u32x4_t*>(bsrc + k0) : zero;
+  constexpr int CHK = 32 * RT_STEPS;
+  const int nchunks = (k_hi - k_lo + CHK - 1) / CHK;
+  // operands of one chunk; 16-byte pieces past k_hi are zero
+  auto load = [&](int c, u32x4_t (&a)[RT_STEPS][2], u32x4_t (&b)[RT_STEPS]) {
+#pragma unroll
+    for (int s = 0; s < RT_STEPS; ++s) {
+      const int k0 = k_lo + c * CHK + 32 * s;
+      b[s] = (k0 + sc * 8 < k_hi) ? *reinterpret_cast<const u32x4_t*>(bsrc + k0) : zero;
+      const bool ok = k0 + kq * 8 < k_hi;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[s][i] = ok ? *reinterpret_cast<const u32x4_t*>(ap[i] + k0) : zero;
+    }
   };
-  u32x4_t bnext = ldb(k_lo);
-  *reinterpret_cast<u32x4_t*>(&bs[0][sdst]) = bnext;
+  auto stage = [&](int buf, const u32x4_t (&b)[RT_STEPS]) {
+#pragma unroll
+    for (int s = 0; s < RT_STEPS; ++s) *reinterpret_cast<u32x4_t*>(&bs[buf][s][sdst]) = b[s];
+  };
+  auto multiply = [&](int buf, const u32x4_t (&a)[RT_STEPS][2]) {
+#pragma unroll
+    for (int s = 0; s < RT_STEPS; ++s) {
+      u32x4_t b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4_t*>(&bs[buf][s][boff[j]]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t pp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, a[s][i]), __builtin_bit_cast(bf16x8_t, b[j]), zero4,
+              0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] += (double)pp[v];
+        }
+    }
+  };
+
+  // chunks alternate between two register sets and two LDS buffers
+  u32x4_t a0[RT_STEPS][2], b0[RT_STEPS], a1[RT_STEPS][2], b1[RT_STEPS];
+  if (nchunks > 0) {
+    load(0, a0, b0);
+    stage(0, b0);
+  }
+  if (nchunks > 1) load(1, a1, b1);
   __syncthreads();
-  int buf = 0;
-  for (int k0 = k_lo; k0 < k_hi; k0 += 32) {
-    const bool more = k0 + 32 < k_hi;
-    if (more) bnext = ldb(k0 + 32);
-    const bool ok = (k0 + kq * 8) < k_hi;
-    u32x4_t a[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = ok ? *reinterpret_cast<const u32x4_t*>(ap[i] + k0) : zero;
-    u32x4_t b[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4_t*>(&bs[buf][boff[j]]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4_t pp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, b[j]), zero4, 0, 0, 0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] += (double)pp[v];
-      }
-    if (more) *reinterpret_cast<u32x4_t*>(&bs[buf ^ 1][sdst]) = bnext;
+  for (int c = 0; c < nchunks; c += 2) {
+    multiply(0, a0);
+    if (c + 1 < nchunks) stage(1, b1);
+    if (c + 2 < nchunks) load(c + 2, a0, b0);
     __syncthreads();
-    buf ^= 1;
+    if (c + 1 >= nchunks) break;
+    multiply(1, a1);
+    if (c + 2 < nchunks) stage(0, b0);
+    if (c + 3 < nchunks) load(c + 3, a1, b1);
+    __syncthreads();
   }
 
   // D layout of the 16x16 output: lane holds column (lane & 15), rows 4*(lane>>4)+v
@@ -177,8 +210,18 @@ __global__ __launch_bounds__(256) void topk_kernel(
     key[j] = -INFINITY;
     sc[j] = 0.0;
     if (e < E) {
+      // the partials are loaded four at a time (independent loads) and added
+      // in split order
       double zz = zpart[t * E + e];
-      for (int q = 1; q < nsplit; ++q) zz += zpart[((int64_t)q * N + t) * E + e];
+      for (int q = 1; q < nsplit; q += 4) {
+        double pq[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pq[i] = (q + i < nsplit) ? zpart[((int64_t)(q + i) * N + t) * E + e] : 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (q + i < nsplit) zz += pq[i];
+      }
       if (logit_bias) zz += (double)logit_bias[e];
       if (z_out) z_out[t * E + e] = zz;
       const double s = sig ? 1.0 / (1.0 + exp(-zz)) : zz;   // sigmoid score, or the logit
@@ -311,7 +354,14 @@ hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* w, double* zpar
   const int ns = (d + len - 1) / len;
   dim3 grid((unsigned)((N + RT_TOK - 1) / RT_TOK), (unsigned)((E + RT_EXP - 1) / RT_EXP),
             (unsigned)ns);
-  router_bf16_kernel<<<grid, 256, 0, s>>>(x, w, zpart, N, d, E, len);
+  // two-step chunks (more loads in flight per wave) while two blocks per CU
+  // hold the whole grid; otherwise one-step chunks at three blocks per CU, so
+  // a large grid still runs in one round
+  const int64_t blocks = (int64_t)grid.x * grid.y * grid.z;
+  if (blocks <= 2 * kCus)
+    router_bf16_kernel<2, 2><<<grid, 256, 0, s>>>(x, w, zpart, N, d, E, len);
+  else
+    router_bf16_kernel<1, 3><<<grid, 256, 0, s>>>(x, w, zpart, N, d, E, len);
   return hipGetLastError();
 }
 

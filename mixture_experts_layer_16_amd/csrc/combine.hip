@@ -33,15 +33,26 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = rows[j];
-      if (r < 0) continue;
-      const float g = gw[j];
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(y_rows + (int64_t)r * d + c * 8);
+    // the rows of up to 8 slots are loaded together, then added in slot order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      u32x4_t v[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = fmaf(g, f16_to_f32((uint16_t)(v[q] & 0xffffu)), acc[2 * q]);
-        acc[2 * q + 1] = fmaf(g, f16_to_f32((uint16_t)(v[q] >> 16)), acc[2 * q + 1]);
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        const int r = j < k ? rows[j] : -1;
+        v[jj] = r >= 0 ? *reinterpret_cast<const u32x4_t*>(y_rows + (int64_t)r * d + c * 8)
+                       : (u32x4_t){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        if (j >= k || rows[j] < 0) continue;
+        const float g = gw[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(g, f16_to_f32((uint16_t)(v[jj][q] & 0xffffu)), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(g, f16_to_f32((uint16_t)(v[jj][q] >> 16)), acc[2 * q + 1]);
+        }
       }
     }
     for (int s = 0; s < S; ++s) {

@@ -1016,20 +1016,7 @@ struct GemmCfg {
 //  * groups averaging at least 128 rows: the direct-to-LDS 256 x 256 kernel
 //    (8 waves for gate/up, 4 for down);
 //  * otherwise 128-row tiles, 4 waves, two blocks per CU.
-#ifdef MOE_DLCFG
-static GemmCfg dl_cfg(int bm, int bk, int ns, int nw) {
-  return GemmCfg{bm, 256, bk, nw / 2, 2, 1, ns, 0, 1};
-}
-#endif
 GemmCfg choose_cfg(const FfnCall& c, int mode) {
-#ifdef MOE_DLCFG
-  if (c.N > 64) return dl_cfg(MOE_DLCFG);
-#endif
-#ifdef MOE_CFG
-  (void)c;
-  (void)mode;
-  return GemmCfg{MOE_CFG};
-#else
   const int64_t groups = c.n_gather + c.n_ident;
   const int64_t rows = c.routed_rows + c.n_ident * c.N;
   const int64_t avg = groups > 0 ? rows / groups : 0;
@@ -1042,7 +1029,6 @@ GemmCfg choose_cfg(const FfnCall& c, int mode) {
   // W_down fragments is amortised over twice the MFMAs)
   if (avg >= 128) return GemmCfg{256, 256, 64, mode == MODE_DOWN ? 2 : 4, 2, 1, 2, 0, 1};
   return GemmCfg{128, 256, 32, 2, 2, 2, 2, 0, 0};
-#endif
 }
 
 // a configuration is usable by a pass if the gate/up fragments pair up
@@ -1076,7 +1062,6 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
     MOE_DL(256, 64, 2, 4)
     MOE_DL(128, 64, 2, 4)
     MOE_DL(256, 64, 2, 8)
-    MOE_DL(256, 32, 3, 8)
     MOE_DL(128, 64, 3, 4)
     return hipErrorInvalidValue;
 #undef MOE_DL
@@ -1089,13 +1074,6 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
     MOE_TRY(128, 256, 32, 2, 2, 2, 2, 0)
     MOE_TRY(32, 256, 64, 1, 4, 2, 2, 0)
     MOE_TRY(32, 128, 64, 1, 4, 2, 2, 0)
-#ifdef MOE_CFG
-#define MOE_TRY_CFG(a, n, b, c, d, e, f, g, h) MOE_TRY(a, n, b, c, d, e, f, g)
-#define MOE_TRY_CFG2(...) MOE_TRY_CFG(__VA_ARGS__)
-    MOE_TRY_CFG2(MOE_CFG)
-#undef MOE_TRY_CFG2
-#undef MOE_TRY_CFG
-#endif
     return hipErrorInvalidValue;
 #undef MOE_TRY
   } else {

@@ -636,7 +636,13 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   // ---- fragment reads: lane supplies row lr of a 32-row fragment and k-chunk
   // 2*kk + lh of the slice; fragment bases are multiples of 32 rows, so the
   // swizzle of the lane's line depends on lr alone
-  const int wm = wave % WM, wn = wave / WM;
+  // Waves w and w+4 share a SIMD.  With 8 waves the row bands are dealt so
+  // that every SIMD holds one wave of rows 0-127 and one of rows 128-255: a
+  // tile with at most 128 valid rows then keeps each SIMD busy with one wave,
+  // while the waves without rows only copy and wait.
+  const int wm = (NW == 8) ? 2 * (wave >> 2) + ((wave & 3) >> 1) : wave % WM;
+  const int wn = (NW == 8) ? (wave & 1) : wave / WM;
+  const bool act = __builtin_amdgcn_readfirstlane(tl.m0 + wm * WROWS < tl.M ? 1 : 0) != 0;
   const int lr = lane & 31, lh = lane >> 5;
   const int lsw = lds_swizzle<RPL>(lr / RPL);
   int a_off[FM], b_off[FN];
@@ -675,9 +681,11 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   // na/nb, when RD) and this MFMA's share of the copies of slice dkt into
   // stage dst (when DMA), so loads and copies issue while the matrix cores
   // are busy and every fragment read has most of a step to land.
-  auto step = [&](auto RD, auto DMA, const u32x4_t (&af)[FM], const u32x4_t (&bf)[FN], int rst,
-                  int rkk, u32x4_t (&na)[FM], u32x4_t (&nb)[FN], int dst, int dkt) {
-    constexpr bool kRd = decltype(RD)::value;
+  // ACT false: a wave without valid rows issues the copies only
+  auto step = [&](auto ACT, auto RD, auto DMA, const u32x4_t (&af)[FM], const u32x4_t (&bf)[FN],
+                  int rst, int rkk, u32x4_t (&na)[FM], u32x4_t (&nb)[FN], int dst, int dkt) {
+    constexpr bool kAct = decltype(ACT)::value;
+    constexpr bool kRd = decltype(RD)::value && kAct;
     // DMA: 0 none, 1 all copies of slice dkt, 2 its first half, 3 its second half
     constexpr int kDma = decltype(DMA)::value;
     constexpr int D0 = (kDma == 3) ? NLD / 2 : 0;
@@ -692,14 +700,16 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
       const int i = m / FN, j = m % FN;
       // weight fragment first: the block of C^T, so each lane ends up with
       // runs of 4 consecutive output columns of one row
-      if (MODE == MODE_DOWN)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(f16x8_t, b[j]), __builtin_bit_cast(f16x8_t, af[i]), acc[i][j], 0,
-            0, 0);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, b[j]), __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j],
-            0, 0, 0);
+      if constexpr (kAct) {
+        if (MODE == MODE_DOWN)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8_t, b[j]), __builtin_bit_cast(f16x8_t, af[i]), acc[i][j],
+              0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, b[j]), __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j],
+              0, 0, 0);
+      }
       if constexpr (kRd) {
 #pragma unroll
         for (int r = 2 * m; r < 2 * m + 2; ++r) {
@@ -742,79 +752,85 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   using D_LO = std::integral_constant<int, 2>;
   using D_HI = std::integral_constant<int, 3>;
 
-  u32x4_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  int st = 0;
-  if constexpr (NS == 2) {
-    // prologue: slices 0 and 1 into stages 0 and 1 (clamped to the last slice:
-    // copies into a stage no slice uses are never read); wait for slice 0
-    issue_slice(0, 0);
-    issue_slice(1, min(1, nsl - 1));
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
-    __syncthreads();
-    read_frags(0, 0, fa0, fb0);
-    convert_b(fb0);
-    // Steady state over slices 0 .. nsl-2 (slice kt in stage kt % 2, its
-    // step-0 fragments already in fa0/fb0).  Steps 0 .. KS-2; then the wait
-    // for slice kt+1 and the barrier that publishes it and frees stage kt % 2;
-    // then the last step of slice kt with the copies of slice kt+2 into the
-    // freed stage and the first fragment reads of slice kt+1 in its shadow.
-    // Copies past the last slice repeat it into a stage never read again.
-    for (int kt = 0; kt + 1 < nsl; ++kt) {
-      const int nx = st ^ 1;
-#pragma unroll
-      for (int kk = 0; kk + 1 < KS; ++kk) {
-        if (kk % 2 == 0) step(T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
-        else step(T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the slice loop, once with the matrix work (waves with rows) and once
+  // without it (copies, waits and barriers only, in the same order)
+  auto slice_loop = [&](auto ACT) {
+    u32x4_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    int st = 0;
+    if constexpr (NS == 2) {
+      // prologue: slices 0 and 1 into stages 0 and 1 (clamped to the last slice:
+      // copies into a stage no slice uses are never read); wait for slice 0
+      issue_slice(0, 0);
+      issue_slice(1, min(1, nsl - 1));
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
       __syncthreads();
-      step(T_{}, D_ALL{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + 2, nsl - 1));
-      st = nx;
+      if constexpr (decltype(ACT)::value) read_frags(0, 0, fa0, fb0);
+      if constexpr (decltype(ACT)::value) convert_b(fb0);
+      // Steady state over slices 0 .. nsl-2 (slice kt in stage kt % 2, its
+      // step-0 fragments already in fa0/fb0).  Steps 0 .. KS-2; then the wait
+      // for slice kt+1 and the barrier that publishes it and frees stage kt % 2;
+      // then the last step of slice kt with the copies of slice kt+2 into the
+      // freed stage and the first fragment reads of slice kt+1 in its shadow.
+      // Copies past the last slice repeat it into a stage never read again.
+      for (int kt = 0; kt + 1 < nsl; ++kt) {
+        const int nx = st ^ 1;
+  #pragma unroll
+        for (int kk = 0; kk + 1 < KS; ++kk) {
+          if (kk % 2 == 0) step(ACT, T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+          else step(ACT, T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        step(ACT, T_{}, D_ALL{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + 2, nsl - 1));
+        st = nx;
+      }
+    } else {
+      // Three or more stages: the refill of a stage is spread over two steps so
+      // the copies never queue up in one.  Slice kt+NS goes into stage kt % NS
+      // in two halves: the first in the last step of slice kt (after the
+      // barrier that frees the stage), the second in step 0 of slice kt+1.  At
+      // the end of slice kt, slices kt+2 .. kt+NS-1 (whole) may still be in
+      // flight.  Prologue: slices 0 .. NS-2 and the first half of slice NS-1.
+  #pragma unroll
+      for (int q = 0; q + 1 < NS; ++q) issue_slice(q, min(q, nsl - 1));
+      {
+        const uint32_t sb = lds_base + (NS - 1) * SB;
+  #pragma unroll
+        for (int j = 0; j < NLD / 2; ++j)
+          g2lds16(src_of(j, min(NS - 1, nsl - 1)), sb + NW * 1024 * j);
+      }
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD + NLD / 2) : "memory");
+      __syncthreads();
+      if constexpr (decltype(ACT)::value) read_frags(0, 0, fa0, fb0);
+      if constexpr (decltype(ACT)::value) convert_b(fb0);
+      int pv = NS - 1;
+      for (int kt = 0; kt + 1 < nsl; ++kt) {
+        const int nx = (st + 1 == NS) ? 0 : st + 1;
+        step(ACT, T_{}, D_HI{}, fa0, fb0, st, 1, fa1, fb1, pv, min(kt + NS - 1, nsl - 1));
+  #pragma unroll
+        for (int kk = 1; kk + 1 < KS; ++kk) {
+          if (kk % 2 == 0) step(ACT, T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+          else step(ACT, T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD) : "memory");
+        __syncthreads();
+        step(ACT, T_{}, D_LO{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + NS, nsl - 1));
+        pv = st;
+        st = nx;
+      }
     }
-  } else {
-    // Three or more stages: the refill of a stage is spread over two steps so
-    // the copies never queue up in one.  Slice kt+NS goes into stage kt % NS
-    // in two halves: the first in the last step of slice kt (after the
-    // barrier that frees the stage), the second in step 0 of slice kt+1.  At
-    // the end of slice kt, slices kt+2 .. kt+NS-1 (whole) may still be in
-    // flight.  Prologue: slices 0 .. NS-2 and the first half of slice NS-1.
-#pragma unroll
-    for (int q = 0; q + 1 < NS; ++q) issue_slice(q, min(q, nsl - 1));
     {
-      const uint32_t sb = lds_base + (NS - 1) * SB;
-#pragma unroll
-      for (int j = 0; j < NLD / 2; ++j)
-        g2lds16(src_of(j, min(NS - 1, nsl - 1)), sb + NW * 1024 * j);
-    }
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD + NLD / 2) : "memory");
-    __syncthreads();
-    read_frags(0, 0, fa0, fb0);
-    convert_b(fb0);
-    int pv = NS - 1;
-    for (int kt = 0; kt + 1 < nsl; ++kt) {
-      const int nx = (st + 1 == NS) ? 0 : st + 1;
-      step(T_{}, D_HI{}, fa0, fb0, st, 1, fa1, fb1, pv, min(kt + NS - 1, nsl - 1));
-#pragma unroll
-      for (int kk = 1; kk + 1 < KS; ++kk) {
-        if (kk % 2 == 0) step(T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
-        else step(T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
+      // last slice (stage st)
+  #pragma unroll
+      for (int kk = 0; kk + 1 < KS; ++kk) {
+        if (kk % 2 == 0) step(ACT, T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
+        else step(ACT, T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
       }
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD) : "memory");
-      __syncthreads();
-      step(T_{}, D_LO{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + NS, nsl - 1));
-      pv = st;
-      st = nx;
+      step(ACT, F_{}, D_NONE{}, fa1, fb1, 0, 0, fa0, fb0, 0, 0);
     }
-  }
-  {
-    // last slice (stage st)
-#pragma unroll
-    for (int kk = 0; kk + 1 < KS; ++kk) {
-      if (kk % 2 == 0) step(T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
-      else step(T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
-    }
-    step(F_{}, D_NONE{}, fa1, fb1, 0, 0, fa0, fb0, 0, 0);
-  }
+  };
+  if (act) slice_loop(T_{});
+  else slice_loop(F_{});
   // no copy may still be writing LDS when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -1109,7 +1125,9 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   const bool split = cfg_up.dl && bm == 256 && cfg_dn.dl && cfg_dn.bm == 256 && G >= 128;
   // remainder tiles: 4 waves; three stages in the gate/up pass (its copies need
   // the deeper prefetch: -4% time for the stage on ds-P and v41), two in the
-  // down pass (three measured +3%)
+  // down pass (three measured +3%).  (Leaving the gate/up remainders in the
+  // main launch as tiles of at most 128 valid rows, which the 8-wave kernel
+  // runs on one wave per SIMD, measured 1-2% slower for the stage.)
   const GemmCfg cfg_s{128, 256, 64, 2, 2, 1, 3, 0, 1};
   const GemmCfg cfg_s_dn{128, 256, 64, 2, 2, 1, 2, 0, 1};
   int32_t* plan_s = split ? c.plan + plan_stride(G) : nullptr;

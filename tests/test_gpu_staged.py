@@ -124,3 +124,36 @@ def test_routing_trace_through_permute():
                 dm = drop.view(N, k).cpu().numpy()
                 assert sorted(int(a) for a, b in zip(*np.nonzero(dm))) == \
                     v["dropped_tokens_at_expert0"]
+
+
+def test_two_streams_at_once():
+    """Two layers enqueued on two streams without a synchronisation between
+    them (each with its own workspace and outputs) give the results of the
+    same calls made one after the other: the library keeps no state between
+    calls and orders all work on the caller's stream."""
+    import parity
+    from mixture_experts_layer_16_amd import _lib as L
+    names = ("cap-s", "ds-s")
+    print("[streams] " + " ".join(names), flush=True)
+    ws_, di_, ref = [], [], []
+    for n in names:
+        w = synth.get(n)
+        di = sdev.upload(synth.make_inputs(w))
+        y, _ = parity.gpu_forward(w, di)
+        ws_.append(w)
+        di_.append(di)
+        ref.append(y)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for w in ws_:
+        p = parity.problem_of(w)
+        outs.append((p, torch.full((w.N, w.d), float("nan"), dtype=torch.float32, device="cuda"),
+                     L.workspace(p)))
+    torch.cuda.synchronize()   # inputs, outputs and workspaces exist before either stream runs
+    for (p, y, ws), di, st in zip(outs, di_, streams):
+        L.moe_forward(p, L.weights(di.w_router, di.w_gate, di.w_up, di.w_down, di.ws_gate,
+                                   di.ws_up, di.ws_down),
+                      di.x, di.logit_bias, di.sel_bias, di.modality, y, None, ws, stream=st)
+    torch.cuda.synchronize()
+    for (_, y, _), yr in zip(outs, ref):
+        assert torch.equal(y, yr)

@@ -204,12 +204,17 @@ def pmc_traffic(kernel: str, workload: str, src_hash: str):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="cap")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--gpus", type=int, default=1,
+                    help="GPUs (one only: the layer runs on one GPU; more exits with a message)")
+    ap.add_argument("--steps", type=int, default=100, help="timed steps")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed steps before them")
+    ap.add_argument("--workload", default="cap",
+                    help="cap (default), mix-P, ds-P, v41, mix-D, ds-D, or a small member "
+                         "of a family (cap-s, mix-s, ds-s, v41-s, ...)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the float64 oracle on the host")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of host time the oracle sample is sized for")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (moe_backward on the forward's routing and "
                          "saved pre-activations) instead of the forward")

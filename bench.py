@@ -3,14 +3,16 @@
 
 A step is one whole layer (router, top-k, dispatch, routed + shared experts,
 combine) over one batch of seeded synthetic tokens already resident in HBM.
-The default workload is the capacity/drop layer (N=16384, d=2048, 64 routed +
-1 shared SwiGLU experts of inner size 1408, top-2, softmax router with a Zipf
-logit skew, C = ceil(N*k/E)).
+The default workload is the largest one-GPU layer, the DeepSeek-V4.1-Flash-
+shaped multimodal layer (N=16384, d=5120, 384 routed + 1 shared SwiGLU experts
+of inner size 2304 clipped at 10, top-6, sigmoid router with one selection-bias
+set per modality, 30% image tokens in contiguous blocks).
 
 Prints one JSON line: tokens/s, ms per step, the roofline entry of the
 dominant kernel (timed with HIP events on the library's stream over the timed
-region) and the float64 CPU oracle timed on a bounded sample on this host.
-Progress goes to stderr.
+region), the per-modality expert load histograms, the GPU clock sampled during
+the timed steps, and the float64 CPU oracle timed on a bounded sample on this
+host.  Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -52,13 +54,18 @@ def algorithmic(w, A, touched, dtype_bytes=2):
     return flops, nbytes, gu_flops, gu_bytes
 
 
-def cpu_baseline(w, inp, budget_s=15.0):
-    """Time the float64 oracle (as it is) on a bounded sample of the workload:
-    routing + dispatch of the whole batch, expert FFNs for a prefix of tokens.
-    Returns the dict for the JSON line."""
-    import numpy as np
-    from oracle import moe_oracle as O
-    import synth
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _blas_info():
     try:
         from threadpoolctl import threadpool_info
         info = threadpool_info()
@@ -66,52 +73,140 @@ def cpu_baseline(w, inp, budget_s=15.0):
         blas = ",".join(sorted({f"{i.get('internal_api')}" for i in info}))
     except Exception:  # pragma: no cover
         threads, blas = len(os.sched_getaffinity(0)), "unknown"
+    return threads, blas
+
+
+def cpu_baseline(w, inp, budget_s=15.0, reps=1, single_thread=False):
+    """Time the float64 oracle (as it is) on a bounded sample of the workload
+    and scale it to the whole layer:
+      * routing + dispatch of the whole batch (timed as they are);
+      * routed experts: a seeded sample of the touched experts runs through the
+        oracle's forward (the routing restricted to them: the others' slots
+        become 'no expert', so the oracle skips them), with each sampled
+        expert's bf16 -> float64 weight upcast timed apart; FFN time is scaled
+        by kept rows, upcast time by touched experts;
+      * shared experts: their upcast, and the oracle on a prefix of the tokens
+        (scaled by N / prefix).
+    Data generation is outside every timed region.  reps > 1 keeps the best of
+    that many measurements; single_thread adds the same estimate with one BLAS
+    thread.  Memory: one sampled expert's float64 weights at a time."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    import synth
+    threads, blas = _blas_info()
     x = synth.to_f64(w, inp.x)
     wr = synth.to_f64(w, inp.w_router)
     lb = None if inp.logit_bias is None else inp.logit_bias.astype(np.float64)
     sb = None if inp.sel_bias is None else inp.sel_bias.astype(np.float64)
-    cache = {}
+    C = O.capacity(w.f, w.N, w.k, w.E)
 
-    def get(e, shared=False):
-        key = (shared, e)
-        if key not in cache:
-            arrs = inp.shared(e) if shared else inp.expert(e)
-            cache[key] = tuple(None if a is None else synth.to_f64(w, a) for a in arrs)
-        return cache[key]
+    def route_once():
+        t0 = time.perf_counter()
+        r = O.route(x, wr, w.k, w.gating, lb, sb, inp.modality)
+        disp = O.dispatch(r["idx"], w.E, C, inp.modality)
+        return time.perf_counter() - t0, r, disp
 
-    t0 = time.perf_counter()
-    r = O.route(x, wr, w.k, w.gating, lb, sb, inp.modality)
-    disp = O.dispatch(r["idx"], w.E, O.capacity(w.f, w.N, w.k, w.E), inp.modality)
-    t_route = time.perf_counter() - t0
-    # warm the per-expert float64 weights outside the timed FFN sample
-    for e in range(w.E):
-        get(e)
-    for s in range(w.S):
-        get(s, True)
+    t_route, r, disp = route_once()
+    rows = np.diff(disp["offsets"]).astype(np.int64)
+    touched = np.nonzero(rows)[0]
+    by_rows = touched[np.argsort(rows[touched], kind="stable")]
+    A = int(rows.sum())
 
-    def ffn_time(n):
-        toks = np.arange(n)
-        t = time.perf_counter()
-        O.forward(x, w.k, w.E, w.gating, w.activation, get_expert=get, n_shared=w.S,
-                  get_shared=lambda s: get(s, True), w_router=wr, clip=w.clip, f=w.f,
-                  logit_bias=lb, sel_bias=sb, modality=inp.modality, forced_idx=r["idx"],
-                  tokens=toks)
-        return time.perf_counter() - t
+    def timed_get(enc, acc):
+        def get(e):
+            t = time.perf_counter()
+            arrs = tuple(None if a is None else synth.to_f64(w, a) for a in enc[e])
+            acc[0] += time.perf_counter() - t
+            return arrs
+        return get
 
-    n = min(w.N, 128)
-    t_probe = ffn_time(n)
-    # forward(tokens=...) also re-routes the whole batch: subtract that part
-    per_tok = max(t_probe - t_route, 1e-6) / n
-    n2 = int(min(w.N, max(n, budget_s / per_tok)))
-    t_ffn = ffn_time(n2)
-    t_tok = max(t_ffn - t_route, 1e-9) / n2 + t_route / w.N
-    return {"value": 1.0 / t_tok, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": (f"float64 NumPy oracle ({blas} BLAS): routing + dispatch of all {w.N} "
-                       f"tokens ({t_route:.2f} s) and expert FFNs + combine for the first {n2} "
-                       f"tokens ({t_ffn - t_route:.2f} s); value = 1 / (route time per token + "
-                       f"FFN time per sampled token)"),
-            "host_cpu_count": len(os.sched_getaffinity(0))}
+    def run(idx, get, n_shared=0, get_shared=None, tokens=None):
+        t0 = time.perf_counter()
+        O.forward(x, w.k, w.E, w.gating, w.activation, get_expert=get, n_shared=n_shared,
+                  get_shared=get_shared, clip=w.clip, f=w.f, modality=inp.modality,
+                  forced_idx=idx, forced_w=r["g"], tokens=tokens)
+        return time.perf_counter() - t0
+
+    none = np.full((w.N, w.k), -1, np.int64)
+
+    def measure(n_exp, n_tok, t_route=t_route):
+        """One estimate of the whole layer's oracle time: n_exp routed experts
+        spread evenly over the touched experts ordered by kept rows (so the
+        sample's rows mirror the layer's), their time scaled by touched /
+        n_exp; the shared experts on the first n_tok tokens, scaled by N /
+        n_tok.  The oracle's per-call work that does not depend on the experts
+        (dispatch, the loop over all E experts' masks) is timed apart, once."""
+        sel = np.unique(np.linspace(0, len(by_rows) - 1, n_exp).round().astype(np.int64))
+        sample = np.sort(by_rows[sel])
+        enc = {int(e): inp.expert(int(e)) for e in sample}        # generated, untimed
+        up = [0.0]
+        t_fixed = run(none, timed_get({}, [0.0]))
+        t_s = run(np.where(np.isin(r["idx"], sample), r["idx"], -1), timed_get(enc, up))
+        scale = len(touched) / len(sample)
+        res = {"route_s": t_route, "fixed_s": t_fixed,
+               "routed_upcast_s": up[0] * scale,
+               "routed_ffn_s": max(t_s - t_fixed - up[0], 0.0) * scale,
+               "shared_upcast_s": 0.0, "shared_ffn_s": 0.0,
+               "sample_s": t_s, "sampled_experts": int(len(sample)),
+               "sampled_rows": int(rows[sample].sum()), "shared_tokens": 0}
+        if w.S:
+            senc = [inp.shared(j) for j in range(w.S)]
+            sup = [0.0]
+            toks = np.arange(n_tok)
+            t_f = run(none, timed_get({}, [0.0]), tokens=toks)
+            t_sh = run(none, timed_get({}, [0.0]), n_shared=w.S,
+                       get_shared=timed_get(dict(enumerate(senc)), sup), tokens=toks)
+            res["shared_upcast_s"] = sup[0]
+            res["shared_ffn_s"] = max(t_sh - t_f - sup[0], 0.0) * w.N / n_tok
+            res["shared_tokens"] = int(n_tok)
+            res["sample_s"] += t_sh
+        res["upcast_s"] = res["routed_upcast_s"] + res["shared_upcast_s"]
+        res["experts_s"] = res["routed_ffn_s"] + res["shared_ffn_s"]
+        res["total_s"] = t_route + t_fixed + res["upcast_s"] + res["experts_s"]
+        return res
+
+    # size the sample from a small probe: about half the budget on routed
+    # experts, a third on the shared experts' token prefix
+    probe = measure(min(2, len(touched)), min(w.N, 128))
+    per_exp = (probe["routed_upcast_s"] + probe["routed_ffn_s"]) / max(len(touched), 1)
+    n_exp = int(min(len(touched), max(2, 0.5 * budget_s / max(per_exp, 1e-6))))
+    n_tok = 0
+    if w.S:
+        per_tok = probe["shared_ffn_s"] / w.N
+        n_tok = int(min(w.N, max(128, budget_s / 3 / max(per_tok, 1e-9))))
+    best = None
+    for _ in range(max(1, reps)):
+        est = measure(n_exp, n_tok)
+        if best is None or est["total_s"] < best["total_s"]:
+            best = est
+    out = {"value": w.N / best["total_s"], "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle", "cpu_model": cpu_model(), "blas": blas,
+           "host_cpu_count": len(os.sched_getaffinity(0)), "best_of": max(1, reps),
+           "route_s": best["route_s"], "upcast_s": best["upcast_s"],
+           "experts_s": best["experts_s"], "fixed_s": best["fixed_s"],
+           "layer_s": best["total_s"], "sample_s": best["sample_s"],
+           "sample": (f"float64 NumPy oracle: routing + dispatch of all {w.N} tokens timed "
+                      f"({best['route_s']:.2f} s); routed experts: {best['sampled_experts']} of "
+                      f"the {len(touched)} touched experts, spread over their row counts "
+                      f"({best['sampled_rows']} of {A} kept rows), through the oracle's forward, "
+                      f"their time scaled by touched / sampled experts, with the bf16->float64 "
+                      f"weight upcasts shown apart ({best['upcast_s']:.2f} s for the layer)"
+                      + (f"; shared expert on the first {best['shared_tokens']} tokens, scaled "
+                         f"by N" if w.S else "")
+                      + f"; value = N / estimated layer time ({best['total_s']:.2f} s; "
+                      f"{best['sample_s']:.1f} s measured on the sample)")}
+    if single_thread:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                t1, _, _ = route_once()
+                st = measure(max(2, n_exp // 16), max(128, n_tok // 16) if w.S else 0, t1)
+            out["single_thread"] = {"value": w.N / st["total_s"], "layer_s": st["total_s"],
+                                    "upcast_s": st["upcast_s"],
+                                    "sampled_experts": st["sampled_experts"]}
+        except Exception as e:  # pragma: no cover
+            out["single_thread"] = {"error": str(e)}
+    return out
 
 
 def cpu_baseline_backward(w, inp, budget_s=15.0):
@@ -170,6 +265,94 @@ def cpu_baseline_backward(w, inp, budget_s=15.0):
             "host_cpu_count": len(os.sched_getaffinity(0))}
 
 
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi, the ROCm system-management
+    library) on a host thread while the timed steps run; reports mean, min and
+    max in MHz, or the reason it could not (then the entry is null)."""
+
+    def __init__(self, period_s=0.005):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._h = None
+        try:
+            import amdsmi
+            self._amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("no GPU handle")
+            self._h = handles[0]
+            if len(handles) > 1:
+                # pick the GPU torch runs on, by PCI address
+                import torch
+                pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+                bus = getattr(pr, "pci_bus_id", None)
+                for h in handles:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                    if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                        self._h = h
+            self.read()
+        except Exception as e:
+            self.error = f"{type(e).__name__}: {e}"
+
+    def read(self):
+        info = self._amdsmi.amdsmi_get_clock_info(self._h, self._amdsmi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self.read())
+            except Exception as e:  # pragma: no cover
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            time.sleep(self.period)
+
+    def start(self):
+        if self.error is None:
+            import threading
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        try:
+            self._amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+        if self.error is not None or not self.samples:
+            return {"mhz_mean": None, "note": self.error or "no samples"}
+        import numpy as np
+        a = np.asarray(self.samples)
+        return {"mhz_mean": float(a.mean()), "mhz_min": float(a.min()), "mhz_max": float(a.max()),
+                "samples": int(a.size), "source": "amdsmi current graphics clock, sampled every "
+                f"{self.period * 1e3:.0f} ms during the timed steps"}
+
+
+def modality_loads(w, counts, mcounts, modality):
+    """Per-modality expert load histograms: demand per expert for text and image
+    tokens, and each expert's share of the modality's assignments."""
+    import numpy as np
+    n_img = int(np.asarray(modality).sum())
+    res = {}
+    for m, name in enumerate(("text", "image")):
+        c = np.asarray(mcounts[m], np.int64)
+        tot = int(c.sum())
+        share = c / tot if tot else np.zeros_like(c, dtype=np.float64)
+        res[name] = {"tokens": (w.N - n_img) if m == 0 else n_img, "assignments": tot,
+                     "counts": c.tolist(), "load_share": [round(float(v), 6) for v in share],
+                     "max_over_mean": float(c.max() * w.E / tot) if tot else 0.0,
+                     "idle_experts": int((c == 0).sum())}
+    res["all"] = {"counts": np.asarray(counts, np.int64).tolist()}
+    return res
+
+
 def roofline_entry(flops, nbytes, ms, traffic):
     """The roofline entry of a launch with the given algorithmic flops and
     bytes: bound by HBM when its flops per byte are below the ridge (peak
@@ -208,8 +391,8 @@ def main():
                     help="GPUs (one only: the layer runs on one GPU; more exits with a message)")
     ap.add_argument("--steps", type=int, default=100, help="timed steps")
     ap.add_argument("--warmup", type=int, default=10, help="untimed steps before them")
-    ap.add_argument("--workload", default="cap",
-                    help="cap (default), mix-P, ds-P, v41, mix-D, ds-D, or a small member "
+    ap.add_argument("--workload", default="v41",
+                    help="v41 (default), cap, mix-P, ds-P, mix-D, ds-D, toy, or a small member "
                          "of a family (cap-s, mix-s, ds-s, v41-s, ...)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the float64 oracle on the host")
@@ -258,7 +441,10 @@ def main():
     y = torch.empty((w.N, w.d), dtype=torch.float32, device="cuda")
     offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
     counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
-    rout = L.routing(offsets=offsets, counts=counts)
+    mcounts = (torch.empty(2 * w.E, dtype=torch.int32, device="cuda")
+               if w.n_bias_sets == 2 else None)
+    sat = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rout = L.routing(offsets=offsets, counts=counts, modality_counts=mcounts, sat_count=sat)
     wts = L.weights(di.w_router, di.w_gate, di.w_up, di.w_down, di.ws_gate, di.ws_up, di.ws_down)
     stream = torch.cuda.current_stream()
 
@@ -282,6 +468,8 @@ def main():
     profs = [L.profile({("gate_up", 0): a, ("gate_up", 1): b}) for a, b in evs]
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    clock = ClockSampler()
+    clock.start()
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(K):
@@ -289,6 +477,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clk = clock.stop()
     ms_step = wall * 1e3 / K
     ms_step_ev = e0.elapsed_time(e1) / K
     gu_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -313,6 +502,16 @@ def main():
     off = offsets.cpu().numpy()
     A = int(off[-1])
     touched = int(np.count_nonzero(np.diff(off)))
+    n_sat = int(sat.cpu().item())
+    if n_sat:
+        log(f"WARNING: {n_sat} fp16 intermediates saturated")
+    loads = None
+    if mcounts is not None:
+        loads = modality_loads(w, counts.cpu().numpy(),
+                               mcounts.cpu().numpy().reshape(2, w.E), inp.modality)
+        log("per-modality load: " + ", ".join(
+            f"{m}: {loads[m]['assignments']} assignments, max/mean {loads[m]['max_over_mean']:.2f}"
+            f", {loads[m]['idle_experts']} idle" for m in ("text", "image")))
     flops, nbytes, gu_flops, gu_bytes = algorithmic(w, A, touched,
                                                     dtype_bytes=2 if w.dtype == "bf16" else 4)
     tokens_s = w.N / (ms_step * 1e-3)
@@ -339,7 +538,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the float64 CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(w, inp, args.cpu_budget)
+        small = w.N <= 64 or w.name in ("cap", "toy") or w.name.endswith("-s")
+        cpu = cpu_baseline(w, inp, args.cpu_budget, reps=3 if small else 1,
+                           single_thread=small)
         log(f"cpu oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
     out = {
@@ -357,14 +558,17 @@ def main():
         "data": "synthetic (seeded; random-init weights of the stated shapes)",
         "config": {"workload": w.name, "N": w.N, "d": w.d, "E": w.E, "S": w.S, "k": w.k,
                    "I": w.I, "capacity_factor": w.f, "gating": w.gating,
-                   "activation": w.activation, "kept_assignments": A,
-                   "touched_experts": touched},
+                   "activation": w.activation, "clip": w.clip,
+                   "n_bias_sets": w.n_bias_sets, "image_frac": w.image_frac,
+                   "kept_assignments": A, "touched_experts": touched},
         "layer": {"tflops": layer_tflops, "mfma_frac": layer_tflops / PEAK_MFMA_TFLOPS,
                   "gbs": layer_gbs, "hbm_frac": layer_gbs / PEAK_HBM_GBS,
                   "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
-                  "ms_per_step_events": ms_step_ev},
+                  "ms_per_step_events": ms_step_ev, "fp16_saturated": n_sat},
         "stages_ms": acc,
         "roofline": roof,
+        "gpu_clock": clk,
+        "modality_load": loads,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -42,7 +42,17 @@
  * - Expert output rows ("y_rows", between moe_expert_ffn and moe_combine) are
  *   IEEE fp16 when p->dtype == MOE_BF16 and float32 when MOE_F32.  Internally
  *   the hidden activation h is fp16 as well and the down projection runs on
- *   the fp16 matrix cores, with the bf16 W_down converted exactly to fp16.
+ *   the fp16 matrix cores, with the bf16 W_down converted to fp16.
+ * - Range of the fp16 intermediates (MOE_BF16 only).  h and the expert rows
+ *   hold magnitudes up to 65504; a larger (or non-finite) value is stored as
+ *   +-65504 -- the layer's result is then wrong for the tokens concerned.
+ *   moe_forward counts such values in routing_out->sat_count (see moe_routing):
+ *   0 means every intermediate was in range.  This happens only with very
+ *   large activations (|x W_gate| |x W_up| beyond ~6.5e4 without a clip); with
+ *   act_clip <= 65504, h cannot overflow.  W_down entries convert exactly
+ *   when 2^-17 <= |w| <= 65504; smaller ones are truncated to multiples of
+ *   2^-24 (absolute error below 6e-8) and larger ones saturate at 65504 --
+ *   a property of the weights the caller can check once.
  * - Weight layout is [out][in] (each row is one output unit, contiguous along
  *   the reduction dimension): router [E][d]; gate/up [E][I][d]; down [E][d][I];
  *   shared experts [S][I][d] and [S][d][I].  For ReLU experts w_gate is NULL,
@@ -141,9 +151,19 @@ typedef struct {
    * then skips recomputing them. */
   void* act_a;
   void* act_u;
+  /* Range status of the fp16 intermediates (device, nullable) int32 [1] out:
+   * set to 0 at the start of the expert stage, then the number of hidden (h)
+   * and expert-row elements that exceeded fp16's range (|v| > 65504 or not
+   * finite) and were saturated.  Non-zero means y is wrong for some tokens;
+   * the caller may rerun in MOE_F32 or rescale x.  Always 0 for MOE_F32. */
+  int32_t* sat_count;
 } moe_routing;
 
-/* Bytes of device workspace any call below needs for problem p (host). */
+/* Bytes of device workspace any call below needs for problem p (host): the
+ * router's float64 logits, the routing arrays of steps 1-3 of "Как устроен
+ * MoE-слой" ("Основы MoE"), the dispatch arrays of the routing slides' trace
+ * ("Cas guidé — trace complète"), and the hidden activations and expert output
+ * rows of every kept assignment and shared-expert row (steps 3-4). */
 int moe_workspace_size(const moe_problem* p, size_t* bytes);
 
 /* Capacity C = ceil(f * N * k / E) computed exactly on the binary value of f;
@@ -191,7 +211,13 @@ int moe_permute(const moe_problem* p, const int32_t* topk_idx, const uint8_t* mo
                 int32_t* row_of, int32_t* token_of_row, uint8_t* drop_mask,
                 void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFNs over grouped rows.
+/* Expert FFNs over grouped rows: step 3 of "Как устроен MoE-слой" ("Основы
+ * MoE": each chosen expert runs on its tokens), with the SwiGLU expert of three
+ * matrices and the clip of the V4.1 page ("Mixture-of-Experts", table "Les
+ * chiffres de DeepSeek-V4.1-Flash" and "Le compte des paramètres") or the
+ * two-layer ReLU expert of the "Mixture of Experts" fiche (code section); the
+ * shared expert ("Mixture-of-Experts : routage et capacité", "L'idée — Top-k et
+ * mélange") is the dense mode.
  * Routed mode (token_of_row != NULL): for each expert e, rows
  *   [offsets[e], offsets[e+1]) take x[token_of_row[row]] and y_rows[row] =
  *   FFN_e(x[token]).  Weights are the routed [E][..] tensors.
@@ -215,9 +241,13 @@ int moe_expert_ffn(const moe_problem* p, const void* x, const int32_t* token_of_
 int moe_combine(const moe_problem* p, const void* y_rows, const int32_t* row_of,
                 const float* topk_w, const void* y_shared, void* y, void* stream);
 
-/* The whole layer: route, permute, routed + shared experts, combine; y is
- * float32 [N][d].  Equal to the staged calls.  routing_out (host struct of device pointers, nullable)
- * receives the intermediate routing arrays for verification. */
+/* The whole layer ("Основы MoE", "Как устроен MoE-слой", steps 1-4, with the
+ * capacity and drop rule of "Mixture-of-Experts : routage et capacité", "L'idée
+ * — Capacité" and "Cas guidé — trace complète", and the shared expert of its
+ * "L'idée — Top-k et mélange"): route, permute, routed + shared experts,
+ * combine; y is float32 [N][d].  Equal to the staged calls.  routing_out (host
+ * struct of device pointers, nullable) receives the intermediate routing
+ * arrays for verification and the range status of the fp16 intermediates. */
 int moe_forward(const moe_problem* p, const moe_weights* w, const void* x,
                 const float* logit_bias, const float* sel_bias, const uint8_t* modality,
                 void* y, const moe_routing* routing_out, void* ws, size_t ws_bytes,

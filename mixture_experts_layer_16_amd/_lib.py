@@ -56,7 +56,8 @@ class Weights(ctypes.Structure):
 class Routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_w", "counts", "modality_counts", "offsets", "row_of",
-                 "token_of_row", "drop_mask", "logits", "final_idx", "act_a", "act_u")]
+                 "token_of_row", "drop_mask", "logits", "final_idx", "act_a", "act_u",
+                 "sat_count")]
 
 
 class Grads(ctypes.Structure):

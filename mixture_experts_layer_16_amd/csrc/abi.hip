@@ -478,6 +478,7 @@ static int forward_impl(const moe_problem* p, const moe_weights* w, const void* 
   c.plan = reinterpret_cast<int32_t*>(base + L.plan);
   c.save_a = r.act_a;
   c.save_u = r.act_u;
+  c.sat = r.sat_count;
   if (prof) {
     for (int i = 0; i < 6; ++i) c.marks[i] = prof->ev[2 * MOE_STAGE_PLAN + i];
   }

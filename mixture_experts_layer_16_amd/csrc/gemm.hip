@@ -33,8 +33,11 @@ enum { MODE_GATEUP = 0, MODE_RELU_UP = 1, MODE_DOWN = 2 };
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(
     const int32_t* __restrict__ offsets, int n_gather, int n_ident, int64_t N,
     int64_t rows_cap, int64_t ident_row0, int BM, int BMS, int32_t* __restrict__ plan,
-    int32_t* __restrict__ plan_s) {
+    int32_t* __restrict__ plan_s, int32_t* __restrict__ sat) {
   __shared__ int32_t mt[2 * 1024];
+  // the range count of this call's fp16 intermediates starts at zero (the
+  // GEMMs that add to it run after this kernel on the same stream)
+  if (sat && threadIdx.x == 0) *sat = 0;
   __shared__ int32_t mts[2 * 1024];
   __shared__ int32_t tmp[1024];
   const int G = n_gather + n_ident;
@@ -184,6 +187,8 @@ struct GemmParams {
   // (SwiGLU) or x W1 before the ReLU
   void* Sa;
   void* Su;
+  int32_t* sat;                  // optional: count of h / y_rows values saturated to
+                                 // fp16's finite range
 };
 
 // ---------------------------------------------------------------------------
@@ -204,7 +209,8 @@ struct GemmParams {
 //
 // Number formats.  The gate/up pass multiplies bf16 x and bf16 weights; its
 // result h is stored in fp16, whose 11-bit significand rounds 8x finer than
-// bf16 (|h| is far inside fp16's range; the conversion saturates at +-65504).
+// bf16 (for inputs of the usual scale |h| is far inside fp16's range; a value
+// beyond +-65504 is saturated and counted in the call's range status).
 // The down pass therefore runs on the fp16 matrix cores: the bf16 W_down tile is
 // converted to fp16 while it is staged into LDS -- exact for every bf16 value in
 // fp16's normal range, and within 2^-24 absolute below it.  Expert output rows
@@ -462,6 +468,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
   // ---- epilogue.  32x32 accumulator layout: element v of a lane is row
   // 8*(v/4) + 4*(lane/32) + v%4, column lane%32.
   uint16_t* C = static_cast<uint16_t*>(p.C);
+  int nsat = 0;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
           if (col < p.Ncols) {
             const float a = acc[i][jn][v];
             const float u = acc[i][jn + FN / 2][v];
-            crow[col] = f32_to_f16_sat(swiglu(a, u, p.clip));
+            crow[col] = f32_to_f16_sat_n(swiglu(a, u, p.clip), nsat);
             if (p.Su) {
               static_cast<uint16_t*>(p.Sa)[(tl.rb + m) * p.ldC + col] = f32_to_f16_sat(a);
               static_cast<uint16_t*>(p.Su)[(tl.rb + m) * p.ldC + col] = saved_up_bits(a, u, p.clip);
@@ -493,12 +500,13 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
             if (MODE == MODE_RELU_UP && p.Su)
               static_cast<uint16_t*>(p.Su)[(tl.rb + m) * p.ldC + col] = f32_to_f16_sat(vv);
             if (MODE == MODE_RELU_UP) vv = fmaxf(vv, 0.f);
-            crow[col] = f32_to_f16_sat(vv);
+            crow[col] = f32_to_f16_sat_n(vv, nsat);
           }
         }
       }
     }
   }
+  if (p.sat && nsat) atomicAdd(p.sat, nsat);
 }
 
 // ---------------------------------------------------------------------------
@@ -847,6 +855,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
     constexpr int RDS = WROWS * HC * 2 / 1024;   // 16-byte reads per lane per pass
     static_assert(NW * WROWS * PS <= NS * SB, "epilogue staging fits the stages");
     char* eb = lds + wave * (WROWS * PS);
+    int nsat = 0;
     // WHAT: 0 = the pass's output (h or the expert row); 1 = the gate
     // pre-activation a (SwiGLU) or the up pre-activation before the ReLU;
     // 2 = the up pre-activation u (SwiGLU)
@@ -861,17 +870,24 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
 #pragma unroll
           for (int vq = 0; vq < 4; ++vq) {
             uint32_t hb[4];   // fp16 bits
+            // the range count covers stored elements only (padding rows and
+            // columns repeat the last valid ones)
+            const int col0 = tl.n0 + wn * WCOLS + pass * HC + 32 * jj + 8 * vq + 4 * lh;
+            const bool row_ok = tl.m0 + wm * WROWS + 32 * i + lr < tl.M;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
+              float h;
               if (MODE == MODE_GATEUP) {
                 const float a = acc[i][jj][4 * vq + c], u = acc[i][jj + 2][4 * vq + c];
-                hb[c] = kWhat == 0 ? f32_to_f16_sat(swiglu(a, u, p.clip))
+                h = swiglu(a, u, p.clip);
+                hb[c] = kWhat == 0 ? f32_to_f16_sat(h)
                                    : (kWhat == 1 ? f32_to_f16_sat(a) : saved_up_bits(a, u, p.clip));
               } else {
-                float h = acc[i][2 * pass + jj][4 * vq + c];
+                h = acc[i][2 * pass + jj][4 * vq + c];
                 if (MODE == MODE_RELU_UP && kWhat == 0) h = fmaxf(h, 0.f);
                 hb[c] = f32_to_f16_sat(h);
               }
+              if (kWhat == 0 && !(fabsf(h) <= 65504.0f) && row_ok && col0 + c < p.Ncols) ++nsat;
             }
             uint2 pk;
             pk.x = hb[0] | (hb[1] << 16);
@@ -904,6 +920,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
         emit(std::integral_constant<int, 1>{}, static_cast<uint16_t*>(p.Su));
       }
     }
+    if (p.sat && nsat) atomicAdd(p.sat, nsat);
   }
 }
 
@@ -1139,7 +1156,7 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   };
   mark(0);
   ffn_plan_kernel<<<1, 1024, 0, s>>>(c.offsets, c.n_gather, c.n_ident, c.N, rows_cap,
-                                     c.identity_row0, bm, 128, c.plan, plan_s);
+                                     c.identity_row0, bm, 128, c.plan, plan_s, c.sat);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   mark(1);
@@ -1161,6 +1178,7 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   up.C = c.h;
   up.Sa = c.save_a;
   up.Su = c.save_u;
+  up.sat = c.dtype == MOE_BF16 ? c.sat : nullptr;
   if (c.activation == MOE_SWIGLU) {
     up.Br0 = c.wg; up.Br1 = c.wu; up.Bs0 = c.sg; up.Bs1 = c.su;
   } else {
@@ -1195,6 +1213,7 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   dn.Br0 = c.wd;
   dn.Bs0 = c.sd;
   dn.C = c.y_rows;
+  dn.sat = c.dtype == MOE_BF16 ? c.sat : nullptr;
   mark(4);
   err = launch_gemm<MODE_DOWN>(dn, c.dtype, cfg_dn, mt, s);
   if (err == hipSuccess && split) {
@@ -1210,7 +1229,7 @@ hipError_t launch_ffn_plan(const int32_t* offsets, int n_gather, int n_ident, in
                            int64_t rows_cap, int64_t ident_row0, int BM, int32_t* plan,
                            hipStream_t s) {
   ffn_plan_kernel<<<1, 1024, 0, s>>>(offsets, n_gather, n_ident, N, rows_cap, ident_row0, BM,
-                                     BM, plan, nullptr);
+                                     BM, plan, nullptr, nullptr);
   return hipGetLastError();
 }
 

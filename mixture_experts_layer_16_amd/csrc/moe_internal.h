@@ -134,6 +134,8 @@ struct FfnCall {
   int32_t* plan;               // workspace for the tile plan
   void* marks[6];              // optional hipEvent_t: before/after plan, gate/up, down
   void *save_a, *save_u;       // optional fp16 [rows][I] pre-activations (bf16 path)
+  int32_t* sat;                // optional: zeroed by the plan, then the count of
+                               // h and y_rows values saturated to fp16's range
 };
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
 // The tile plan alone (BM-row tiles, no remainder plan), for other grouped GEMMs.
@@ -209,6 +211,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
   f = fminf(fmaxf(f, -65504.0f), 65504.0f);
   return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// the same, counting in n the values outside fp16's finite range (saturated)
+__device__ __forceinline__ uint16_t f32_to_f16_sat_n(float f, int& n) {
+  n += (fabsf(f) <= 65504.0f) ? 0 : 1;   // NaN counts as well
+  return f32_to_f16_sat(f);
 }
 __device__ __forceinline__ float f16_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);

@@ -99,6 +99,16 @@ SMALL = {
                      seed=14),
     "relu-bf16-s": replace(WORKLOADS["cap"], name="relu-bf16-s", N=300, d=192, E=6, k=2,
                            I=264, S=1, f=1.25, activation="relu", zipf_offset=0.0, seed=15),
+    # many experts averaging more than 256 rows, with a skewed spread (one empty
+    # expert, ~60 above 256 rows, remainders past the last 256-row tile both
+    # below and above 128 rows): the grouped-GEMM tile plan of the DeepSeek-
+    # and V4.1-shaped prefill layers at a size the oracle runs in seconds
+    "ds-split-s": replace(WORKLOADS["ds-P"], name="ds-split-s", N=6000, d=320, E=160, k=8,
+                          I=200, seed=16),
+    # the V4.1-shaped small layer with the activation clip lowered to 0.06, so
+    # that the clamp is active on a large share of the hidden elements
+    "v41-clip-s": replace(WORKLOADS["v41"], name="v41-clip-s", N=1100, d=320, E=96, k=6,
+                          I=144, clip=0.06, seed=14),
 }
 
 ALL = {**WORKLOADS, **SMALL}

@@ -58,6 +58,7 @@ def alloc_routing(w, dev="cuda"):
         drop_mask=torch.full((max(1, N * k),), 7, dtype=torch.uint8, device=dev),
         logits=torch.full((max(1, N * E),), np.nan, dtype=torch.float64, device=dev),
         final_idx=torch.full((max(1, N * k),), -7, dtype=i32, device=dev),
+        sat_count=torch.full((1,), -7, dtype=i32, device=dev),
     )
 
 
@@ -280,6 +281,9 @@ def full_check(w, inp=None, di=None, tokens=None, report=None, balance=True):
     gidx = check_route(ors, g, report)
     check_dispatch(ors, g, gidx, report)
     check_layer(ors, y, gidx, report, tokens=tokens)
+    # every fp16 intermediate of these inputs is inside fp16's range
+    report["sat_count"] = int(g["sat_count"][0])
+    assert report["sat_count"] == 0, report
     if balance:
         check_balance(ors, out, g, di, report)
     return report, y, g, di

@@ -349,6 +349,33 @@ def test_saved_activation_pointers_are_validated(L):
     assert lib.moe_backward(B(p), B(w), fake, B(rb), fake, B(g), fake, 1 << 40, None) == -1
 
 
-def test_routing_struct_matches_the_header_layout(L):
-    assert ctypes.sizeof(L.Routing) == 12 * 8
-    assert L.Routing.act_u.offset == 88
+def test_structs_match_the_header_layout(L, tmp_path):
+    """sizeof and every field offset of the binding's structs equal what a C
+    compiler makes of include/moe.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"moe_problem": L.Problem, "moe_weights": L.Weights, "moe_routing": L.Routing,
+               "moe_grads": L.Grads, "moe_profile": L.Profile}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "moe.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, *_ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True,
+                             text=True).stdout.splitlines():
+        cname, field, val = ln.split()
+        got[(cname, field)] = int(val)
+    for cname, py in structs.items():
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for fname, *_ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)

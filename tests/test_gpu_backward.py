@@ -217,11 +217,9 @@ def test_backward_with_saved_activations(name):
 
 
 def _workload(name):
-    # v41-clip-s: the V4.1-shaped small layer with the clip lowered to 0.06 so
+    # v41-clip-s is the V4.1-shaped small layer with the clip lowered to 0.06 so
     # that about 30% of silu(a) u are clamped (at 10, none are in the small
     # layer)
-    if name == "v41-clip-s":
-        return synth.derive(synth.get("v41-s"), name=name, clip=0.06)
     return synth.get(name)
 
 

@@ -28,6 +28,109 @@ def test_forward_parity_small(name):
     _say(f"[parity] {name} {rep}")
 
 
+def test_split_tile_plan_all_tokens():
+    """Every token of a layer whose per-expert row counts take every branch of
+    the prefill grouped GEMM's tile plan (more than 128 groups averaging more
+    than 128 rows: 256-row tiles, the remainders past a group's last full tile
+    -- at most 128 rows and more than 128 --, groups smaller than one tile and
+    an empty group) against the oracle: the shape class of the DeepSeek- and
+    V4.1-shaped prefill layers, small enough for the oracle."""
+    import parity
+    w = synth.get("ds-split-s")
+    G = w.E + w.S
+    assert w.N > 64 and G >= 128 and (w.N * w.k + w.N * w.S) // G >= 128
+    rep, y, g, _ = parity.full_check(w)
+    m = np.diff(g["offsets"].astype(np.int64))
+    rem = m % 256
+    classes = {"empty": int((m == 0).sum()), "two_or_more_full_tiles": int((m >= 512).sum()),
+               "rem_le_128": int(((m > 256) & (rem > 0) & (rem <= 128)).sum()),
+               "rem_gt_128": int(((m > 256) & (rem > 128)).sum()),
+               "below_128": int(((m > 0) & (m <= 128)).sum()),
+               "between_128_256": int(((m > 128) & (m < 256)).sum())}
+    _say(f"[parity] ds-split-s row classes {classes} {rep}")
+    assert all(v > 0 for v in classes.values()), classes
+
+
+def test_clamped_bf16_forward_all_tokens():
+    """The bf16 forward with the SwiGLU clamp active on a large share of the
+    hidden elements (clip 0.06 on the V4.1-shaped small layer), every token
+    against the oracle."""
+    import parity
+    from oracle import moe_oracle as O
+    w = synth.get("v41-clip-s")
+    inp = synth.make_inputs(w)
+    # share of the shared expert's hidden elements the clamp changes
+    x = synth.to_f64(w, inp.x)
+    wg, wu, _ = (synth.to_f64(w, a) for a in inp.shared(0))
+    frac = float(np.mean(np.abs(O.silu(x @ wg.T) * (x @ wu.T)) > w.clip))
+    assert frac > 0.1, frac
+    rep, *_ = parity.full_check(w, inp=inp)
+    _say(f"[parity] v41-clip-s clamped share {frac:.3f} {rep}")
+
+
+def _scaled_x_inputs(w, s):
+    """The workload's inputs with x multiplied by 2^s (exact in bf16), and the
+    oracle's largest |h| and |expert output row| over every routed and shared
+    expert on all tokens."""
+    from oracle import moe_oracle as O
+    inp = synth.make_inputs(w)
+    inp.x = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(inp.x) * np.float32(2.0 ** s))
+    x = synth.to_f64(w, inp.x)
+    hmax = ymax = 0.0
+    for arrs in [inp.expert(e) for e in range(w.E)] + [inp.shared(j) for j in range(w.S)]:
+        wg, wu, wd = (synth.to_f64(w, a) for a in arrs)
+        h = O.silu(x @ wg.T) * (x @ wu.T)
+        hmax = max(hmax, float(np.abs(h).max()))
+        ymax = max(ymax, float(np.abs(h @ wd.T).max()))
+    return inp, hmax, ymax
+
+
+def test_fp16_range_large_but_in_range():
+    """x scaled by 2^7: hidden values up to about 2e4, still inside fp16's
+    range -- the layer matches the oracle and reports no saturation."""
+    import parity
+    w = synth.derive(synth.get("mix-s"), name="mix-s-x128")
+    inp, hmax, ymax = _scaled_x_inputs(w, 7)
+    assert 4000 < hmax < 65504 / 1.5 and ymax < 65504 / 1.5, (hmax, ymax)
+    rep, *_ = parity.full_check(w, inp=inp, balance=False)
+    _say(f"[range] in range: max|h| {hmax:.0f} max|row| {ymax:.0f} {rep}")
+
+
+def test_fp16_range_overflow_is_reported():
+    """x scaled by 2^8: some |h| exceed 65504, so the fp16 intermediates
+    saturate; the forward must say so through routing_out->sat_count, with at
+    least as many saturated values as the oracle's hidden values beyond the
+    range (the expert rows computed from them may add more)."""
+    import parity
+    from oracle import moe_oracle as O
+    w = synth.derive(synth.get("mix-s"), name="mix-s-x256")
+    inp, hmax, ymax = _scaled_x_inputs(w, 8)
+    assert hmax > 65504 * 1.01, hmax
+    di = sdev.upload(inp)
+    y, out = parity.gpu_forward(w, di)
+    g = parity.to_np(out)
+    sat = int(g["sat_count"][0])
+    # the oracle's hidden values beyond the range, on the GPU's routing
+    x = synth.to_f64(w, inp.x)
+    idx = g["topk_idx"].reshape(w.N, w.k)
+    n_lo = n_hi = 0
+    for e in range(w.E):
+        rows = np.nonzero((idx == e).any(axis=1))[0]
+        wg, wu, _ = (synth.to_f64(w, a) for a in inp.expert(e))
+        h = np.abs(O.silu(x[rows] @ wg.T) * (x[rows] @ wu.T))
+        n_lo += int((h > 65504 * (1 + 1e-4)).sum())
+        n_hi += int((h > 65504 * (1 - 1e-4)).sum())
+    for j in range(w.S):
+        wg, wu, _ = (synth.to_f64(w, a) for a in inp.shared(j))
+        h = np.abs(O.silu(x @ wg.T) * (x @ wu.T))
+        n_lo += int((h > 65504 * (1 + 1e-4)).sum())
+        n_hi += int((h > 65504 * (1 - 1e-4)).sum())
+    rows_total = (w.N * w.k + w.N * w.S)
+    _say(f"[range] overflow: max|h| {hmax:.0f}, GPU count {sat}, oracle h beyond {n_lo}")
+    assert n_lo > 0
+    assert n_lo <= sat <= n_hi + rows_total * w.d
+
+
 def test_capacity_drops_really_happen():
     import parity
     w = synth.get("cap-s")

@@ -570,3 +570,23 @@ def test_hash_router_properties():
         z ^= z >> 31
         assert unmix(z) == v
         assert O.hash_route([v], E, 1)[0][0, 0] == z % E
+
+
+def test_hash_router_published_outputs():
+    """The mixer against the published outputs of Vigna's splitmix64 generator
+    (tests/golden/splitmix64.json): from the state 0 the generator's j-th output
+    mixes the state j * increment, so the oracle's hash of the token id
+    (j - 1) * increment (as a signed 64-bit id) must be that output modulo E.
+    Several moduli (one near 2^63) check nearly every bit of the word."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "splitmix64.json")))
+    inc = int(g["increment"], 16)
+    M = (1 << 64) - 1
+    for j, out in enumerate(g["outputs"]):
+        state = (int(g["state0"]) + j * inc) & M
+        tid = state - (1 << 64) if state >= (1 << 63) else state   # as int64
+        want = int(out, 16)
+        for E in (384, 1 << 30, (1 << 63) - 25):
+            idx, _ = O.hash_route(np.array([tid], np.int64), E, 1)
+            assert int(idx[0, 0]) == want % E, (j, E)

@@ -81,7 +81,9 @@ enum {
   MOE_ERR_INVALID = -2,       /* a size or option is out of range */
   MOE_ERR_UNSUPPORTED = -3,   /* valid but not supported (alignment, dtype mix) */
   MOE_ERR_WORKSPACE = -4,     /* workspace smaller than moe_workspace_size() */
-  MOE_ERR_HIP = -5            /* a kernel launch failed (hipGetLastError) */
+  MOE_ERR_HIP = -5,           /* a kernel launch failed (hipGetLastError) */
+  MOE_ERR_TOO_LARGE = -6      /* moe_forward_noalloc: the problem needs more than
+                                 MOE_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_gating;
@@ -278,6 +280,28 @@ int moe_forward_routed(const moe_problem* p, const moe_weights* w, const void* x
  *   topk_w (device) float32 [N*k] out. */
 int moe_route_hash(const moe_problem* p, const int64_t* token_ids, int32_t* topk_idx,
                    float* topk_w, void* stream);
+
+/* Bytes of the fixed device scratch of moe_forward_noalloc: the most
+ * workspace (moe_workspace_size) a problem may need to run through it. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same layer, the same kernels and the same results, with no workspace
+ * argument and no allocation of any kind.  Its scratch is a file-scope device
+ * array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) in the library, one copy per GPU
+ * the library runs on, held until the process ends; the first call on a
+ * device looks up that device's copy.  Problems whose moe_workspace_size
+ * exceeds it return MOE_ERR_TOO_LARGE before anything is enqueued (64 MiB
+ * holds decode batches and prefills of a few hundred tokens at the named
+ * shapes).  Every call on one GPU shares that GPU's scratch, and its contents
+ * stay from the last call: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.  Arguments
+ * and results as for moe_forward. */
+int moe_forward_noalloc(const moe_problem* p, const moe_weights* w, const void* x,
+                        const float* logit_bias, const float* sel_bias,
+                        const uint8_t* modality, void* y, const moe_routing* routing_out,
+                        void* stream);
 
 /* Stages of moe_forward, in launch order (indices into moe_profile.ev). */
 enum {

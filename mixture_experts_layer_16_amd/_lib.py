@@ -21,13 +21,15 @@ MOE_OVERFLOW_DROP, MOE_OVERFLOW_REROUTE = 0, 1
 MOE_SWIGLU, MOE_RELU = 0, 1
 MOE_BF16, MOE_F32 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_INVALID", -3: "MOE_ERR_UNSUPPORTED",
-          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
+          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_TOO_LARGE"}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 # every function include/moe.h declares
 EXPORTS = ("moe_workspace_size", "moe_capacity", "moe_param_counts", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex",
            "moe_balance", "moe_forward_routed", "moe_route_hash", "moe_backward_workspace_size",
-           "moe_backward", "moe_backward_ex", "moe_status_string", "moe_version")
+           "moe_backward", "moe_backward_ex", "moe_status_string", "moe_version",
+           "moe_forward_noalloc")
 STAGES = ("route", "permute", "plan", "gate_up", "down", "combine")
 BSTAGES = ("prep", "recompute", "dh", "rows", "wgrad", "dx")
 
@@ -90,6 +92,8 @@ def _load() -> ctypes.CDLL:
         "moe_forward_ex": [P, ctypes.POINTER(Weights), V, V, V, V, V, ctypes.POINTER(Routing),
                            ctypes.POINTER(Profile), V, ctypes.c_size_t, V],
         "moe_balance": [P, V, V, V, V, V, V, V, ctypes.c_float, V, ctypes.c_size_t, V],
+        "moe_forward_noalloc": [P, ctypes.POINTER(Weights), V, V, V, V, V,
+                                ctypes.POINTER(Routing), V],
         "moe_forward_routed": [P, ctypes.POINTER(Weights), V, V, V, V, V,
                                ctypes.POINTER(Routing), V, ctypes.c_size_t, V],
         "moe_route_hash": [P, V, V, V, V],
@@ -329,6 +333,17 @@ def moe_forward(p, w: Weights, x, logit_bias, sel_bias, modality, y, routing_out
     if raw:
         return st
     _check("moe_forward", st)
+
+
+def moe_forward_noalloc(p, w: Weights, x, logit_bias, sel_bias, modality, y, routing_out=None,
+                        stream=None, raw=False):
+    """moe_forward on the library's fixed per-GPU scratch (no workspace)."""
+    rout = ctypes.byref(routing_out) if routing_out is not None else None
+    st = LIB.moe_forward_noalloc(ctypes.byref(p), ctypes.byref(w), ptr(x), ptr(logit_bias),
+                                 ptr(sel_bias), ptr(modality), ptr(y), rout, _stream(stream))
+    if raw:
+        return st
+    _check("moe_forward_noalloc", st)
 
 
 def profile(events: dict, stages=STAGES) -> Profile:

@@ -3,7 +3,15 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
+
+// Scratch of the allocation-free entry point (moe_forward_noalloc): one copy
+// per GPU, held until the process ends.  Host code never uses this name as an
+// address (on the host it is a stand-in, not device memory): it uses the
+// device address hipGetSymbolAddress returns, kept per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace moe {
 
@@ -503,6 +511,43 @@ int moe_forward_ex(const moe_problem* p, const moe_weights* w, const void* x,
                       ws_bytes, stream, nullptr, nullptr);
 }
 
+// The current device's copy of the scratch array, looked up once per device
+// (thread-safe); NULL with *status set if the lookup fails.
+static void* noalloc_scratch(int* status) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = MOE_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      *status = MOE_ERR_HIP;
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+int moe_forward_noalloc(const moe_problem* p, const moe_weights* w, const void* x,
+                        const float* logit_bias, const float* sel_bias,
+                        const uint8_t* modality, void* y, const moe_routing* routing_out,
+                        void* stream) {
+  int st = validate(p);
+  if (st) return st;
+  if (ws_layout(p).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+  void* ws = noalloc_scratch(&st);
+  if (!ws) return st;
+  return forward_impl(p, w, x, logit_bias, sel_bias, modality, y, routing_out, nullptr, ws,
+                      MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr);
+}
+
 int moe_forward_routed(const moe_problem* p, const moe_weights* w, const void* x,
                        const int32_t* topk_idx, const float* topk_w, const uint8_t* modality,
                        void* y, const moe_routing* routing_out, void* ws, size_t ws_bytes,
@@ -606,6 +651,8 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported (alignment or option)";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP kernel launch failed";
+    case MOE_ERR_TOO_LARGE:
+      return "problem needs more than the 64 MiB fixed scratch of moe_forward_noalloc";
     default: return "unknown status";
   }
 }

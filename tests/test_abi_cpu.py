@@ -44,7 +44,7 @@ def test_header_and_exports_agree(L):
 
 def test_version_and_status_strings(L):
     assert "gfx950" in L.moe_version()
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.moe_status_string(code) != "unknown status"
     assert L.moe_status_string(7) == "unknown status"
 
@@ -379,3 +379,21 @@ def test_structs_match_the_header_layout(L, tmp_path):
         assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
         for fname, *_ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch_before_any_launch(L):
+    """moe_forward_noalloc checks the problem's workspace against its fixed
+    scratch on the host, before touching the device: a V4.1-shaped batch of
+    2048 tokens needs more than 64 MiB and is refused with MOE_ERR_TOO_LARGE;
+    invalid problems still return their validation status first."""
+    fake = 1 << 20
+    w = L.Weights(fake, fake, fake, fake, fake, fake, fake)
+    big = L.problem(2048, 5120, 384, 6, 2304, S=1, gating="sigmoid", n_bias_sets=2,
+                    act_clip=10.0)
+    assert L.moe_workspace_size(big) > L.NOALLOC_SCRATCH_BYTES
+    st = L.LIB.moe_forward_noalloc(ctypes.byref(big), ctypes.byref(w), fake, None, fake, fake,
+                                   fake, None, None)
+    assert st == -6
+    bad = L.problem(16, 5120, 384, 0, 2304)
+    assert L.LIB.moe_forward_noalloc(ctypes.byref(bad), ctypes.byref(w), fake, None, None, None,
+                                     fake, None, None) == -2

@@ -266,42 +266,43 @@ def cpu_baseline_backward(w, inp, budget_s=15.0):
 
 
 class ClockSampler:
-    """Samples the GPU's graphics clock (amdsmi, the ROCm system-management
-    library) on a host thread while the timed steps run; reports mean, min and
-    max in MHz, or the reason it could not (then the entry is null)."""
+    """Samples the GPU's graphics clock on a host thread while the timed steps
+    run: the current level of the driver's sclk table (sysfs pp_dpm_sclk, the
+    entry marked '*', in MHz).  Reports mean, min and max, or why it could not
+    (then mhz_mean is null)."""
 
     def __init__(self, period_s=0.005):
+        import glob
         import threading
         self.period = period_s
         self.samples = []
         self.error = None
         self._stop = threading.Event()
         self._thread = None
-        self._h = None
+        self.path = None
         try:
-            import amdsmi
-            self._amdsmi = amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            if not handles:
-                raise RuntimeError("no GPU handle")
-            self._h = handles[0]
-            if len(handles) > 1:
-                # pick the GPU torch runs on, by PCI address
+            paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+            if not paths:
+                raise RuntimeError("no pp_dpm_sclk in sysfs")
+            self.path = paths[0]
+            if len(paths) > 1:
+                # the GPU torch runs on, by PCI bus number
                 import torch
                 pr = torch.cuda.get_device_properties(torch.cuda.current_device())
                 bus = getattr(pr, "pci_bus_id", None)
-                for h in handles:
-                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
-                    if bus is not None and int(bdf.split(":")[1], 16) == bus:
-                        self._h = h
+                for q in paths:
+                    addr = os.path.basename(os.path.realpath(os.path.dirname(q)))
+                    if bus is not None and int(addr.split(":")[1], 16) == bus:
+                        self.path = q
             self.read()
         except Exception as e:
             self.error = f"{type(e).__name__}: {e}"
 
     def read(self):
-        info = self._amdsmi.amdsmi_get_clock_info(self._h, self._amdsmi.AmdSmiClkType.GFX)
-        return float(info["clk"])
+        for ln in open(self.path).read().splitlines():
+            if ln.rstrip().endswith("*"):
+                return float(ln.split(":", 1)[1].strip().split("M")[0])
+        raise RuntimeError("no current level marked")
 
     def _run(self):
         while not self._stop.is_set():
@@ -322,17 +323,14 @@ class ClockSampler:
         if self._thread is not None:
             self._stop.set()
             self._thread.join()
-        try:
-            self._amdsmi.amdsmi_shut_down()
-        except Exception:
-            pass
         if self.error is not None or not self.samples:
             return {"mhz_mean": None, "note": self.error or "no samples"}
         import numpy as np
         a = np.asarray(self.samples)
         return {"mhz_mean": float(a.mean()), "mhz_min": float(a.min()), "mhz_max": float(a.max()),
-                "samples": int(a.size), "source": "amdsmi current graphics clock, sampled every "
-                f"{self.period * 1e3:.0f} ms during the timed steps"}
+                "samples": int(a.size),
+                "source": f"{self.path} (current sclk level), sampled every "
+                          f"{self.period * 1e3:.0f} ms during the timed steps"}
 
 
 def modality_loads(w, counts, mcounts, modality):

@@ -125,10 +125,10 @@ static size_t route_partials_bytes(const moe_problem* p) {
   return (size_t)route_splits(p) * (size_t)p->n_tokens * p->n_experts * 8;
 }
 
-static int run_route(const moe_problem* p, const void* x, const void* w_router,
-                     const float* logit_bias, const float* sel_bias, const uint8_t* modality,
-                     int32_t* idx, float* w, double* zpart, double* z_out, hipStream_t s,
-                     int32_t* alt = nullptr) {
+// The router's logits as float64 partial sums in zpart; returns the number of
+// partials, or 0 if the launch failed.
+static int run_router(const moe_problem* p, const void* x, const void* w_router, double* zpart,
+                      hipStream_t s) {
   const int64_t N = p->n_tokens;
   hipError_t err;
   int used = 1;
@@ -142,10 +142,19 @@ static int run_route(const moe_problem* p, const void* x, const void* w_router,
     err = launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
                             zpart, N, p->d_model, p->n_experts, s);
   }
-  if (err != hipSuccess) return MOE_ERR_HIP;
-  err = launch_topk(zpart, used, logit_bias, z_out, p->n_bias_sets ? sel_bias : nullptr, modality,
-                    p->n_bias_sets, p->gating, p->renormalize, idx, w, alt, N, p->n_experts,
-                    p->top_k, s);
+  return err == hipSuccess ? used : 0;
+}
+
+static int run_route(const moe_problem* p, const void* x, const void* w_router,
+                     const float* logit_bias, const float* sel_bias, const uint8_t* modality,
+                     int32_t* idx, float* w, double* zpart, double* z_out, hipStream_t s,
+                     int32_t* alt = nullptr) {
+  const int used = run_router(p, x, w_router, zpart, s);
+  if (!used) return MOE_ERR_HIP;
+  const hipError_t err =
+      launch_topk(zpart, used, logit_bias, z_out, p->n_bias_sets ? sel_bias : nullptr, modality,
+                  p->n_bias_sets, p->gating, p->renormalize, idx, w, alt, p->n_tokens,
+                  p->n_experts, p->top_k, s);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -437,32 +446,6 @@ static int forward_impl(const moe_problem* p, const moe_weights* w, const void* 
   };
   const bool reroute = p->overflow == MOE_OVERFLOW_REROUTE;
   int32_t* alt = reinterpret_cast<int32_t*>(base + L.alt);
-  mark(2 * MOE_STAGE_ROUTE);
-  if (!forced_idx) {
-    st = run_route(p, x, w->w_router, logit_bias, sel_bias, modality, const_cast<int32_t*>(idx),
-                   const_cast<float*>(gw), zpart, r.logits, s, reroute ? alt : nullptr);
-    if (st) return st;
-  }
-  mark(2 * MOE_STAGE_ROUTE + 1);
-  mark(2 * MOE_STAGE_PERMUTE);
-  hipError_t perr;
-  if (reroute) {
-    perr = launch_permute_reroute(
-        idx, alt, modality, counts, mcounts, offsets, row_of, tor, drop, r.final_idx,
-        reinterpret_cast<int32_t*>(base + L.lrank), reinterpret_cast<int32_t*>(base + L.blk_counts),
-        reinterpret_cast<int32_t*>(base + L.cand), reinterpret_cast<int32_t*>(base + L.lrank2),
-        reinterpret_cast<int32_t*>(base + L.blk2), reinterpret_cast<int32_t*>(base + L.kept1), N,
-        p->n_experts, p->top_k, capacity_of(p), s);
-  } else {
-    perr = launch_permute(idx, modality, counts, mcounts, offsets, row_of, tor, drop,
-                          reinterpret_cast<int32_t*>(base + L.lrank),
-                          reinterpret_cast<int32_t*>(base + L.blk_counts), N, p->n_experts,
-                          p->top_k, capacity_of(p), s);
-    if (perr == hipSuccess && r.final_idx)
-      perr = launch_final_idx(idx, row_of, r.final_idx, N * p->top_k, s);
-  }
-  if (perr != hipSuccess) return MOE_ERR_HIP;
-  mark(2 * MOE_STAGE_PERMUTE + 1);
 
   const size_t esz = p->dtype == MOE_BF16 ? 2 : 4;
   FfnCall c{};
@@ -490,11 +473,74 @@ static int forward_impl(const moe_problem* p, const moe_weights* w, const void* 
   if (prof) {
     for (int i = 0; i < 6; ++i) c.marks[i] = prof->ev[2 * MOE_STAGE_PLAN + i];
   }
+
+  if (N <= kSmallTokens && !reroute) {
+    // small batch: router and top-k, then dispatch and the tile plan in one launch
+    mark(2 * MOE_STAGE_ROUTE);
+    if (!forced_idx) {
+      st = run_route(p, x, w->w_router, logit_bias, sel_bias, modality,
+                     const_cast<int32_t*>(idx), const_cast<float*>(gw), zpart, r.logits, s);
+      if (st) return st;
+    }
+    mark(2 * MOE_STAGE_ROUTE + 1);
+    mark(2 * MOE_STAGE_PERMUTE);
+    SmallDispatch sd{};
+    sd.idx = idx;
+    sd.modality = modality;
+    sd.counts = counts;
+    sd.mod_counts = mcounts;
+    sd.offsets = offsets;
+    sd.row_of = row_of;
+    sd.token_of_row = tor;
+    sd.final_idx = r.final_idx;
+    sd.drop = drop;
+    sd.C = capacity_of(p);
+    sd.N = N;
+    sd.E = p->n_experts;
+    sd.k = p->top_k;
+    sd.n_ident = p->n_shared;
+    sd.ident_row0 = c.identity_row0;
+    sd.BM = ffn_plan_rows(c);
+    sd.plan = c.plan;
+    sd.sat = r.sat_count;
+    if (launch_dispatch_small(sd, s) != hipSuccess) return MOE_ERR_HIP;
+    mark(2 * MOE_STAGE_PERMUTE + 1);
+    c.plan_ready = 1;
+  } else {
+    mark(2 * MOE_STAGE_ROUTE);
+    if (!forced_idx) {
+      st = run_route(p, x, w->w_router, logit_bias, sel_bias, modality, const_cast<int32_t*>(idx),
+                     const_cast<float*>(gw), zpart, r.logits, s, reroute ? alt : nullptr);
+      if (st) return st;
+    }
+    mark(2 * MOE_STAGE_ROUTE + 1);
+    mark(2 * MOE_STAGE_PERMUTE);
+    hipError_t perr;
+    if (reroute) {
+      perr = launch_permute_reroute(
+          idx, alt, modality, counts, mcounts, offsets, row_of, tor, drop, r.final_idx,
+          reinterpret_cast<int32_t*>(base + L.lrank),
+          reinterpret_cast<int32_t*>(base + L.blk_counts),
+          reinterpret_cast<int32_t*>(base + L.cand), reinterpret_cast<int32_t*>(base + L.lrank2),
+          reinterpret_cast<int32_t*>(base + L.blk2), reinterpret_cast<int32_t*>(base + L.kept1),
+          N, p->n_experts, p->top_k, capacity_of(p), s);
+    } else {
+      perr = launch_permute(idx, modality, counts, mcounts, offsets, row_of, tor, drop,
+                            reinterpret_cast<int32_t*>(base + L.lrank),
+                            reinterpret_cast<int32_t*>(base + L.blk_counts), N, p->n_experts,
+                            p->top_k, capacity_of(p), s);
+      if (perr == hipSuccess && r.final_idx)
+        perr = launch_final_idx(idx, row_of, r.final_idx, N * p->top_k, s);
+    }
+    if (perr != hipSuccess) return MOE_ERR_HIP;
+    mark(2 * MOE_STAGE_PERMUTE + 1);
+  }
   if (launch_ffn(c, s) != hipSuccess) return MOE_ERR_HIP;
 
-  const void* y_shared = p->n_shared ? static_cast<const void*>(base + L.yrows +
-                                                                (size_t)N * p->top_k * p->d_model * esz)
-                                     : nullptr;
+  const void* y_shared =
+      p->n_shared ? static_cast<const void*>(base + L.yrows +
+                                             (size_t)N * p->top_k * p->d_model * esz)
+                  : nullptr;
   mark(2 * MOE_STAGE_COMBINE);
   if (launch_combine(p->dtype, base + L.yrows, row_of, gw, y_shared, N, p->n_shared, y, N,
                      p->d_model, p->top_k, s) != hipSuccess)

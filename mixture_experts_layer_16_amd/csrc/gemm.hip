@@ -1139,7 +1139,8 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   // and one half tile rather than two full ones.  Only with many groups: the
   // second launch needs enough remainder tiles to fill the chip (measured:
   // -3% time with 257 or 385 groups, +8% with 65).
-  const bool split = cfg_up.dl && bm == 256 && cfg_dn.dl && cfg_dn.bm == 256 && G >= 128;
+  const bool split =
+      !c.plan_ready && cfg_up.dl && bm == 256 && cfg_dn.dl && cfg_dn.bm == 256 && G >= 128;
   // remainder tiles: 4 waves; three stages in the gate/up pass (its copies need
   // the deeper prefetch: -4% time for the stage on ds-P and v41), two in the
   // down pass (three measured +3%).  (Leaving the gate/up remainders in the
@@ -1155,10 +1156,13 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
     if (c.marks[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(c.marks[i]), s);
   };
   mark(0);
-  ffn_plan_kernel<<<1, 1024, 0, s>>>(c.offsets, c.n_gather, c.n_ident, c.N, rows_cap,
-                                     c.identity_row0, bm, 128, c.plan, plan_s, c.sat);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (!c.plan_ready) {
+    ffn_plan_kernel<<<1, 1024, 0, s>>>(c.offsets, c.n_gather, c.n_ident, c.N, rows_cap,
+                                       c.identity_row0, bm, 128, c.plan, plan_s, c.sat);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   mark(1);
 
   GemmParams up{};
@@ -1223,6 +1227,10 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   }
   mark(5);
   return err;
+}
+
+int ffn_plan_rows(const FfnCall& c) {
+  return c.dtype == MOE_BF16 ? choose_cfg(c, MODE_GATEUP).bm : kF32BM;
 }
 
 hipError_t launch_ffn_plan(const int32_t* offsets, int n_gather, int n_ident, int64_t N,

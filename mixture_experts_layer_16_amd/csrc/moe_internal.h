@@ -24,6 +24,7 @@ constexpr int kCus = 256;             // MI355X: compute units (32 per die)
 constexpr int kMaxRouterSplits = 32;  // split-K pieces of the router for small batches
 constexpr int kBalTokens = 64;        // tokens per block of the balance-statistics kernel
 constexpr int kBalMaxBlocks = 512;    // blocks (and partial rows) of that kernel at most
+constexpr int kSmallTokens = 64;      // batches up to this size route and dispatch in one block
 
 // ---------------------------------------------------------------------------
 // device workspace layout (byte offsets from the workspace base)
@@ -90,6 +91,25 @@ hipError_t launch_topk(const double* zpart, int nsplit, const float* logit_bias,
 hipError_t launch_hash_route(const int64_t* ids, int64_t N, int E, int k, int32_t* idx,
                              float* w, hipStream_t s);
 
+// Small batches (N <= kSmallTokens, drop policy): demand histograms, capacity,
+// ranks, permutation and the grouped-GEMM tile plan (BM-row tiles, no
+// remainder plan) in one single-block launch, after the top-k.
+struct SmallDispatch {
+  const int32_t* idx;               // [N*k] the routing (expert of each assignment)
+  const uint8_t* modality;          // nullable (required with mod_counts)
+  int32_t *counts, *mod_counts, *offsets, *row_of, *token_of_row, *final_idx;
+  uint8_t* drop;
+  int64_t C;                        // capacity, < 0 unlimited
+  int64_t N;
+  int E, k;
+  int n_ident;                      // shared experts (dense groups of the plan)
+  int64_t ident_row0;               // first row of the dense groups
+  int BM;                           // tile rows of the grouped GEMMs
+  int32_t* plan;                    // tile plan out
+  int32_t* sat;                     // nullable: range count, zeroed here
+};
+hipError_t launch_dispatch_small(const SmallDispatch& a, hipStream_t s);
+
 hipError_t launch_permute(const int32_t* idx, const uint8_t* modality, int32_t* counts,
                           int32_t* mod_counts, int32_t* offsets, int32_t* row_of,
                           int32_t* token_of_row, uint8_t* drop, int32_t* lrank,
@@ -136,8 +156,12 @@ struct FfnCall {
   void *save_a, *save_u;       // optional fp16 [rows][I] pre-activations (bf16 path)
   int32_t* sat;                // optional: zeroed by the plan, then the count of
                                // h and y_rows values saturated to fp16's range
+  int plan_ready;              // 1: the tile plan (and the zeroed sat) are already in
+                               // `plan` (written by the small-batch dispatch)
 };
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
+// Rows per tile of the grouped GEMMs' tile plan for this call.
+int ffn_plan_rows(const FfnCall& c);
 // The tile plan alone (BM-row tiles, no remainder plan), for other grouped GEMMs.
 hipError_t launch_ffn_plan(const int32_t* offsets, int n_gather, int n_ident, int64_t N,
                            int64_t rows_cap, int64_t ident_row0, int BM, int32_t* plan,

@@ -319,7 +319,122 @@ __global__ __launch_bounds__(256) void final_idx_kernel(const int32_t* __restric
   if (a < nk) final_idx[a] = row_of[a] >= 0 ? idx[a] : -1;
 }
 
+// ---------------------------------------------------------------------------
+// Small batches (N <= kSmallTokens): the demand histograms, capacity,
+// token-order ranks, the permutation and the grouped-GEMM tile plan in one
+// block of 1024 threads, instead of the rank, scan, scatter and plan launches
+// -- with a handful of tokens each of those is mostly start-up latency.  The
+// results equal the separate kernels' (ranks by the same rule: an assignment's
+// rank is the number of earlier assignments, in token-major order, to its
+// expert).
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(SmallDispatch a) {
+  __shared__ int32_t sidx[kSmallTokens * kMaxTopK];
+  __shared__ int32_t srank[kSmallTokens * kMaxTopK];
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t mcnt[2 * kMaxExperts];
+  __shared__ int32_t kept[kMaxExperts];
+  __shared__ int32_t mt[2 * 1024];
+  __shared__ int32_t tmp[1024];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int E = a.E, k = a.k;
+  const int64_t N = a.N;
+  const int NK = (int)(N * k);
+  for (int e = tid; e < E; e += 1024) {
+    cnt[e] = 0;
+    mcnt[e] = 0;
+    mcnt[E + e] = 0;
+  }
+  for (int i = tid; i < NK; i += 1024) sidx[i] = a.idx[i];
+  __syncthreads();
+  // 1. token-order ranks and demand: one wave walks the assignments in order,
+  // 64 at a time; lanes naming the same expert find each other with one
+  // ballot per bit of the expert index
+  if (wave == 0) {
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int c0 = 0; c0 < NK; c0 += 64) {
+      const int i = c0 + lane;
+      const int e = i < NK ? sidx[i] : -1;
+      const bool valid = e >= 0 && e < E;
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool on = valid && ((e >> bit) & 1);
+        const uint64_t m = __ballot(on);
+        peers &= on ? m : ~m;
+      }
+      if (valid) {
+        const int before = __popcll(peers & lt_mask);
+        const int old = cnt[e];
+        if (before == 0) cnt[e] = old + __popcll(peers);
+        srank[i] = old + before;
+        if (a.mod_counts) atomicAdd(&mcnt[(a.modality[i / k] ? 1 : 0) * E + e], 1);
+      }
+    }
+  }
+  __syncthreads();
+  // 2. demand out, kept = min(demand, C), offsets = exclusive prefix sums
+  for (int e = tid; e < E; e += 1024) {
+    const int c = cnt[e];
+    a.counts[e] = c;
+    if (a.mod_counts) {
+      a.mod_counts[e] = mcnt[e];
+      a.mod_counts[E + e] = mcnt[E + e];
+    }
+    kept[e] = (a.C < 0 || c < a.C) ? c : (int)a.C;
+  }
+  __syncthreads();
+  const int A = block_exclusive_scan_1024(kept, E, tmp);
+  for (int e = tid; e < E; e += 1024) a.offsets[e] = kept[e];
+  if (tid == 0) a.offsets[E] = A;
+  // 3. the permutation (kept[] now holds the offsets)
+  for (int i = tid; i < NK; i += 1024) {
+    const int e = sidx[i];
+    int row = -1;
+    if (e >= 0 && e < E && (a.C < 0 || srank[i] < a.C)) {
+      row = kept[e] + srank[i];
+      a.token_of_row[row] = i / k;
+    }
+    a.row_of[i] = row;
+    a.drop[i] = row < 0 ? 1 : 0;
+    if (a.final_idx) a.final_idx[i] = row < 0 ? -1 : e;
+  }
+  // 4. tile plan of the grouped GEMMs: the routed groups' rows from the
+  // offsets, then one dense group of N rows per shared expert
+  const int G = E + a.n_ident;
+  int32_t* tile_start = a.plan;
+  int32_t* row_begin = a.plan + G + 1;
+  int32_t* rows = row_begin + G;
+  for (int g = tid; g < G; g += 1024) {
+    int rb, r;
+    if (g < E) {
+      rb = kept[g];
+      r = (g + 1 < E ? kept[g + 1] : A) - rb;
+    } else {
+      rb = (int)(a.ident_row0 + (int64_t)(g - E) * N);
+      r = (int)N;
+    }
+    row_begin[g] = rb;
+    rows[g] = r;
+    mt[g] = (r + a.BM - 1) / a.BM;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan_1024(mt, G, tmp);
+  for (int g = tid; g < G; g += 1024) tile_start[g] = mt[g];
+  if (tid == 0) {
+    tile_start[G] = total;
+    if (a.sat) *a.sat = 0;   // the range count of this call starts at zero
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dispatch_small(const SmallDispatch& a, hipStream_t s) {
+  dispatch_small_kernel<<<1, 1024, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 int64_t perm_blocks(int64_t N) { return (N + kPermTokens - 1) / kPermTokens; }
 

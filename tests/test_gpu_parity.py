@@ -155,6 +155,11 @@ EDGE = {
                             toy_draws=False),
     "f32-sigmoid-2bias": dict(base="toy-s", gating="sigmoid", n_bias_sets=2, image_frac=0.3,
                               N=300, toy_draws=False),
+    # batches of at most 64 tokens route and dispatch in one launch
+    "small-batch-two-bias-sets": dict(base="v41-s", N=40),
+    "small-batch-drops": dict(base="cap-s", N=48, f=0.5),
+    "small-batch-64": dict(base="ds-s", N=64),
+    "small-batch-raw-weights": dict(base="mixd-s", N=30, renormalize=False),
 }
 
 

@@ -5,8 +5,10 @@
 // nothing, without renormalising the others: "Mixture-of-Experts : routage et
 // capacité", "L'idée — Top-k et mélange" and "Cas guidé — trace complète").
 //
-// One block per token; 128-bit loads and stores; float32 sums in a fixed order
-// (j = 0..k-1, then shared experts); the output is float32.
+// One block per token; 128-bit loads and stores; the expert rows are read once,
+// with non-temporal loads, while y is stored normally (the caller reads it
+// next); float32 sums in a fixed order (j = 0..k-1, then shared experts); the
+// output is float32.
 #include "moe_internal.h"
 
 namespace moe {
@@ -40,7 +42,8 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(
       for (int jj = 0; jj < 8; ++jj) {
         const int j = j0 + jj;
         const int r = j < k ? rows[j] : -1;
-        v[jj] = r >= 0 ? *reinterpret_cast<const u32x4_t*>(y_rows + (int64_t)r * d + c * 8)
+        v[jj] = r >= 0 ? __builtin_nontemporal_load(
+                             reinterpret_cast<const u32x4_t*>(y_rows + (int64_t)r * d + c * 8))
                        : (u32x4_t){0u, 0u, 0u, 0u};
       }
 #pragma unroll
@@ -56,8 +59,8 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(
       }
     }
     for (int s = 0; s < S; ++s) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
-          y_shared + ((int64_t)s * sh_stride_rows + t) * d + c * 8);
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+          y_shared + ((int64_t)s * sh_stride_rows + t) * d + c * 8));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc[2 * q] += f16_to_f32((uint16_t)(v[q] & 0xffffu));

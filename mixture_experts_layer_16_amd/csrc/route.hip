@@ -204,24 +204,39 @@ __global__ __launch_bounds__(256) void topk_kernel(
 
   double key[J], sc[J];
   uint32_t valid = 0;
+  // the logits: split-K partials added in split order.  The partials of all J
+  // key slots are loaded QB splits at a time (J * QB independent loads in
+  // flight), so a batch of tokens split many ways waits for one memory round
+  // trip per QB splits rather than per slot and QB splits
+  constexpr int QB = J <= 4 ? 4 : (J <= 8 ? 2 : 1);
+  double zsum[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + 64 * j;
+    zsum[j] = e < E ? zpart[t * E + e] : 0.0;
+  }
+  for (int q = 1; q < nsplit; q += QB) {
+    double pq[J][QB];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+#pragma unroll
+      for (int i = 0; i < QB; ++i)
+        pq[j][i] = (e < E && q + i < nsplit) ? zpart[((int64_t)(q + i) * N + t) * E + e] : 0.0;
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int i = 0; i < QB; ++i)
+        if (q + i < nsplit) zsum[j] += pq[j][i];
+  }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
     key[j] = -INFINITY;
     sc[j] = 0.0;
     if (e < E) {
-      // the partials are loaded four at a time (independent loads) and added
-      // in split order
-      double zz = zpart[t * E + e];
-      for (int q = 1; q < nsplit; q += 4) {
-        double pq[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pq[i] = (q + i < nsplit) ? zpart[((int64_t)(q + i) * N + t) * E + e] : 0.0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (q + i < nsplit) zz += pq[i];
-      }
+      double zz = zsum[j];
       if (logit_bias) zz += (double)logit_bias[e];
       if (z_out) z_out[t * E + e] = zz;
       const double s = sig ? 1.0 / (1.0 + exp(-zz)) : zz;   // sigmoid score, or the logit

@@ -155,9 +155,11 @@ typedef struct {
   void* act_u;
   /* Range status of the fp16 intermediates (device, nullable) int32 [1] out:
    * set to 0 at the start of the expert stage, then the number of hidden (h)
-   * and expert-row elements that exceeded fp16's range (|v| > 65504 or not
-   * finite) and were saturated.  Non-zero means y is wrong for some tokens;
-   * the caller may rerun in MOE_F32 or rescale x.  Always 0 for MOE_F32. */
+   * and expert-row elements stored as +-65504, fp16's largest magnitude: every
+   * element that exceeded the range (|v| > 65504 or not finite) and was
+   * saturated, plus any in-range one that rounds there (65488 < |v| <= 65504).
+   * Non-zero means y may be wrong for some tokens; the caller may rerun in
+   * MOE_F32 or rescale x.  Always 0 for MOE_F32. */
   int32_t* sat_count;
 } moe_routing;
 

@@ -187,8 +187,8 @@ struct GemmParams {
   // (SwiGLU) or x W1 before the ReLU
   void* Sa;
   void* Su;
-  int32_t* sat;                  // optional: count of h / y_rows values saturated to
-                                 // fp16's finite range
+  int32_t* sat;                  // optional: count of stored h / y_rows values of
+                                 // magnitude 65504 (saturated, or rounded there)
 };
 
 // ---------------------------------------------------------------------------
@@ -210,7 +210,8 @@ struct GemmParams {
 // Number formats.  The gate/up pass multiplies bf16 x and bf16 weights; its
 // result h is stored in fp16, whose 11-bit significand rounds 8x finer than
 // bf16 (for inputs of the usual scale |h| is far inside fp16's range; a value
-// beyond +-65504 is saturated and counted in the call's range status).
+// beyond +-65504 is saturated, and every stored +-65504 is counted in the call's
+// range status).
 // The down pass therefore runs on the fp16 matrix cores: the bf16 W_down tile is
 // converted to fp16 while it is staged into LDS -- exact for every bf16 value in
 // fp16's normal range, and within 2^-24 absolute below it.  Expert output rows
@@ -894,10 +895,6 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
 #pragma unroll
           for (int vq = 0; vq < 4; ++vq) {
             uint32_t hb[4];   // fp16 bits
-            // the range count covers stored elements only (padding rows and
-            // columns repeat the last valid ones)
-            const int col0 = tl.n0 + wn * WCOLS + pass * HC + 32 * jj + 8 * vq + 4 * lh;
-            const bool row_ok = tl.m0 + wm * WROWS + 32 * i + lr < tl.M;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               float h;
@@ -911,7 +908,6 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
                 if (MODE == MODE_RELU_UP && kWhat == 0) h = fmaxf(h, 0.f);
                 hb[c] = f32_to_f16_sat(h);
               }
-              if (kWhat == 0 && !(fabsf(h) <= 65504.0f) && row_ok && col0 + c < p.Ncols) ++nsat;
             }
             uint2 pk;
             pk.x = hb[0] | (hb[1] << 16);
@@ -928,8 +924,14 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
         const u32x4_t val = *reinterpret_cast<const u32x4_t*>(eb + row * PS + c8 * 16);
         const int m = tl.m0 + wm * WROWS + row;
         const int col = tl.n0 + wn * WCOLS + pass * HC + c8 * 8;
-        if (m < tl.M && col < p.Ncols)
+        if (m < tl.M && col < p.Ncols) {
           *reinterpret_cast<u32x4_t*>(C + (tl.rb + m) * p.ldC + col) = val;
+          // the range count reads the stored bits (padding rows and columns,
+          // which repeat the last valid ones, are not stored)
+          if constexpr (kWhat == 0)
+            nsat += f16x2_at_limit(val[0]) + f16x2_at_limit(val[1]) + f16x2_at_limit(val[2]) +
+                    f16x2_at_limit(val[3]);
+        }
       }
     }
     };

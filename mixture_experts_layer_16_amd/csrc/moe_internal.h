@@ -155,7 +155,7 @@ struct FfnCall {
   void* marks[6];              // optional hipEvent_t: before/after plan, gate/up, down
   void *save_a, *save_u;       // optional fp16 [rows][I] pre-activations (bf16 path)
   int32_t* sat;                // optional: zeroed by the plan, then the count of
-                               // h and y_rows values saturated to fp16's range
+                               // stored h and y_rows values of magnitude 65504
   int plan_ready;              // 1: the tile plan (and the zeroed sat) are already in
                                // `plan` (written by the small-batch dispatch)
 };
@@ -236,10 +236,17 @@ __device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
   f = fminf(fmaxf(f, -65504.0f), 65504.0f);
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
-// the same, counting in n the values outside fp16's finite range (saturated)
+// How many of the two fp16 values packed in w have fp16's largest magnitude,
+// 65504: every saturated value (beyond the range, or NaN, which the clamp
+// sends to -65504) and the in-range ones that round there (|v| > 65488).
+__device__ __forceinline__ int f16x2_at_limit(uint32_t w) {
+  return ((w & 0x7fffu) == 0x7bffu) + (((w >> 16) & 0x7fffu) == 0x7bffu);
+}
+// f32_to_f16_sat, adding to n when the result has magnitude 65504 (as above)
 __device__ __forceinline__ uint16_t f32_to_f16_sat_n(float f, int& n) {
-  n += (fabsf(f) <= 65504.0f) ? 0 : 1;   // NaN counts as well
-  return f32_to_f16_sat(f);
+  const uint16_t b = f32_to_f16_sat(f);
+  n += (b & 0x7fffu) == 0x7bffu;
+  return b;
 }
 __device__ __forceinline__ float f16_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);

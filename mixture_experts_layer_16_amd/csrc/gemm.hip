@@ -1122,14 +1122,20 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks <= 0) return hipSuccess;
   if (dtype == MOE_BF16 && cfg.dl) {
-#define MOE_DL(a, b, n, w)                                                        \
-  if (cfg.bm == a && cfg.bk == b && cfg.nsets == n && 2 * cfg.wm == w)            \
-    ffn_gemm_dl<MODE, a, b, n, w><<<(unsigned)blocks, 64 * w, 0, s>>>(gp);       \
-  else
-    MOE_DL(256, 64, 2, 4)
-    MOE_DL(128, 64, 2, 4)
-    MOE_DL(256, 64, 2, 8)
-    MOE_DL(128, 64, 3, 4)
+    // the instances launch_ffn plans: gate/up 256 rows on 8 waves and 128-row
+    // remainders on 4 waves with three stages; down 4 waves with two stages
+    constexpr bool up = MODE != MODE_DOWN;
+#define MOE_DL(a, b, n, w, used)                                                  \
+  if (cfg.bm == a && cfg.bk == b && cfg.nsets == n && 2 * cfg.wm == w) {          \
+    if constexpr (used)                                                           \
+      ffn_gemm_dl<MODE, a, b, n, w><<<(unsigned)blocks, 64 * w, 0, s>>>(gp);     \
+    else                                                                          \
+      return hipErrorInvalidValue;                                                \
+  } else
+    MOE_DL(256, 64, 2, 8, up)
+    MOE_DL(128, 64, 3, 4, up)
+    MOE_DL(256, 64, 2, 4, !up)
+    MOE_DL(128, 64, 2, 4, !up)
     return hipErrorInvalidValue;
 #undef MOE_DL
   } else if (dtype == MOE_BF16) {

@@ -517,7 +517,7 @@ def main():
     layer_gbs = nbytes / (ms_step * 1e-3) / 1e9
     src = open(os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc", "gemm.hip"), "rb").read()
     src_hash = hashlib.sha256(src).hexdigest()
-    # the gate/up grouped GEMM (ffn_gemm_dl<GATEUP, 256, 64, 2> for prefill,
+    # the gate/up grouped GEMM (ffn_gemm_dl<GATEUP, 256, 8> for prefill,
     # ffn_gemm_bf16<GATEUP, 32, ...> for decode batches)
     kname = "ffn_gemm_gate_up"
     traffic = pmc_traffic(kname, w.name, src_hash)

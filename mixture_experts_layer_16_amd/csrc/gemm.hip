@@ -548,10 +548,13 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
 //    consecutive 128-byte lines (1 KiB); each lane picks the global 16-byte
 //    chunk whose swizzled position is its own, so the LDS image equals the
 //    swizzled layout without passing through registers;
-//  * NS LDS stages.  With two, the loads of slice kt+2 are issued right after
-//    the barrier that ends slice kt, while the last 16-wide step of slice kt
-//    is still multiplying, and the first fragments of slice kt+1 are read in
-//    the same shadow, so the matrix cores keep running across the barrier.
+//  * the k-slices' token rows have two LDS stages and their weight rows three.
+//    The weight rows of slice kt+2 are copied during the first two 16-wide
+//    steps of slice kt and its token rows right after the barrier that ends
+//    slice kt, while the last step of slice kt is still multiplying; the first
+//    fragments of slice kt+1 are read in the same shadow, so the matrix cores
+//    keep running across the barrier, and no step issues more than half a
+//    slice's copies.
 // In the down pass the bf16 W_down fragments are converted to fp16 after
 // they are read from LDS (the data never passes through registers before),
 // in the shadow of the preceding step's matrix instructions.
@@ -572,33 +575,28 @@ __device__ __forceinline__ void g2lds16(const void* src, uint32_t lds_base) {
 // the end of a ragged last slice.
 __device__ const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
 
-template <int MODE, int BM, int BK, int NS, int NW>
+template <int MODE, int BM, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   constexpr int BN = 256;
+  constexpr int BK = 64;                     // k-slice: one 128-byte LDS line per staged row
   constexpr int KCH = BK / 8;                // 16-byte chunks per staged row
-  constexpr int RPL = 8 / KCH;               // rows per 128-byte LDS line
   constexpr int KS = BK / 16;                // 16-wide steps per slice
   constexpr int ROWS = BM + BN;              // staged rows per slice
-  constexpr int LINES = ROWS / RPL;          // 128-byte lines per stage
-  constexpr int NLD = LINES / (8 * NW);      // copy instructions per thread per slice
+  constexpr int NLD = ROWS / (8 * NW);       // copy instructions per thread per slice
+  constexpr int JA = NLD * BM / ROWS;        // of which into token rows (then weight rows)
   constexpr int WM = NW / 2;                 // waves along the rows (2 along the columns)
   constexpr int WROWS = BM / WM;
   constexpr int FM = WROWS / 32, FN = 4;
   constexpr int CT = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   constexpr int WCOLS = CT / 2;
-  constexpr int SB = LINES * 128;            // bytes per stage
-  constexpr int SA = BM / RPL * 128;         // bytes of a stage's token rows
-  constexpr int JA = NLD * BM / ROWS;        // copies per thread into those rows
-  // 256-row gate/up tiles with 64-wide slices: the token rows keep two stages
-  // and the weight rows three (2 x 32 + 3 x 32 KiB), so the weight copies are
-  // issued two slices ahead (measured: gate/up stage 0.3-3% faster; the down
-  // pass, whose tiles convert W_down in registers, was 1-3% slower with it)
-  constexpr bool W3 = (NS == 2 && BM == 256 && BK == 64 && MODE != MODE_DOWN);
-  constexpr int SBW = SB - SA;               // bytes of a stage's weight rows
-  constexpr int LDSB = W3 ? 2 * SA + 3 * SBW : NS * SB;
+  // LDS: two stages of token rows and three of weight rows (a slice's token
+  // rows are copied one slice ahead, its weight rows two slices ahead)
+  constexpr int SA = BM * 128;               // bytes of one stage of token rows
+  constexpr int SW = BN * 128;               // bytes of one stage of weight rows
+  constexpr int LDSB = 2 * SA + 3 * SW;
   static_assert(BM % 64 == 0 && BM <= 256 && (NW == 4 || NW == 8) && WROWS >= 32, "tile rows");
-  static_assert((BK == 32 || BK == 64) && NS >= 2 && (NS - 1) * NLD <= 63, "pipeline shape");
-  static_assert(KS % 2 == 0, "steps alternate between two fragment sets");
+  static_assert(JA * 8 * NW == BM && 2 * NLD <= 63, "copies per thread");
+  static_assert(KS == 4, "slice steps");
   static_assert(LDSB <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) char lds[LDSB];
 
@@ -618,23 +616,17 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   const uint32_t lds_base =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * 1024;
 
-  // ---- loaders: copy instruction j of wave w fills stage lines (NW*j + w) * 8
-  // .. + 7; lane i writes line L = (NW*j + w) * 8 + i/8 at position i%8, which
-  // holds logical chunk c = (i%8) ^ swizzle(L) of the line: row L*RPL + c/KCH,
-  // k-chunk c%KCH.  swizzle(L) depends on i/8 (and for one row per line on w).
+  // ---- loaders: staged row r of a slice (token rows 0 .. BM-1, then weight
+  // rows) is the 128-byte LDS line r of its part.  Copy instruction j of wave w
+  // fills rows (NW*j + w) * 8 .. + 7; lane i writes row L = (NW*j + w) * 8 + i/8
+  // at position i%8, which holds k-chunk (i%8) ^ swizzle(L); swizzle(L) depends
+  // on i/8 and on w.
   const int lline = lane >> 3;
-  const int lpos = lane & 7;
-  int gchunk, rsub;
-  {
-    const int sw = (RPL == 1) ? (lline ^ (wave & 1)) : lds_swizzle<2>(lline);
-    const int c = lpos ^ sw;
-    gchunk = c % KCH;
-    rsub = c / KCH;                           // 0 for one row per line
-  }
+  const int gchunk = (lane & 7) ^ lline ^ (wave & 1);
   const char* src[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
-    const int r = ((NW * j + wave) * 8 + lline) * RPL + rsub;
+    const int r = (NW * j + wave) * 8 + lline;
     if (r < BM) {
       int m = tl.m0 + r;
       if (m >= tl.M) m = tl.M - 1;
@@ -669,16 +661,11 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
     const bool ok = kt < nfull || kt * BK + gchunk * 8 < p.K;
     return ok ? src[j] + (int64_t)kt * BK * 2 : reinterpret_cast<const char*>(kZeroChunk);
   };
-  // copy j of a slice: token-row copies (j < JA) go to the part at ca, weight
-  // copies to the part at cb
+  // copy j of a slice: token-row copies (j < JA) of slice ka go to the stage
+  // at LDS address ca, weight-row copies of slice kb to the stage at cb
   auto copy_one = [&](int j, uint32_t ca, uint32_t cb, int ka, int kb) {
     if (j < JA) g2lds16(src_of(j, ka), ca + NW * 1024 * j);
     else g2lds16(src_of(j, kb), cb + NW * 1024 * (j - JA));
-  };
-  auto issue_slice = [&](int st, int kt) {
-    const uint32_t sb = lds_base + st * SB;
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) copy_one(j, sb, sb + SA, kt, kt);
   };
 
   // ---- fragment reads: lane supplies row lr of a 32-row fragment and k-chunk
@@ -692,10 +679,10 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   const int wn = (NW == 8) ? (wave & 1) : wave / WM;
   const bool act = __builtin_amdgcn_readfirstlane(tl.m0 + wm * WROWS < tl.M ? 1 : 0) != 0;
   const int lr = lane & 31, lh = lane >> 5;
-  const int lsw = lds_swizzle<RPL>(lr / RPL);
+  const int lsw = lds_swizzle<1>(lr);
   int a_off[FM], b_off[FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) a_off[i] = ((wm * WROWS + 32 * i + lr) / RPL) * 128;
+  for (int i = 0; i < FM; ++i) a_off[i] = (wm * WROWS + 32 * i + lr) * 128;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     int base;
@@ -703,11 +690,11 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
       base = (j >> 1) * CT + wn * WCOLS + 32 * (j & 1);
     else
       base = wn * WCOLS + 32 * j;
-    b_off[j] = ((base + lr) / RPL) * 128;      // within the stage's weight rows
+    b_off[j] = (base + lr) * 128;              // within a stage of weight rows
   }
   int kq[KS];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) kq[kk] = (((lr % RPL) * KCH + 2 * kk + lh) ^ lsw) * 16;
+  for (int kk = 0; kk < KS; ++kk) kq[kk] = ((2 * kk + lh) ^ lsw) * 16;
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -717,17 +704,14 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // W3 layout: offsets of the token rows and the weight rows of slice kt
+  // LDS offsets of the token rows and of the weight rows of slice kt
   auto ra_of = [&](int kt) { return (kt & 1) * SA; };
-  auto rb_of = [&](int kt) { return 2 * SA + (kt % 3) * SBW; };
-  auto read_frags2 = [&](int ra, int rb, int kk, u32x4_t (&af)[FM], u32x4_t (&bf)[FN]) {
+  auto rb_of = [&](int kt) { return 2 * SA + (kt % 3) * SW; };
+  auto read_frags = [&](int ra, int rb, int kk, u32x4_t (&af)[FM], u32x4_t (&bf)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(lds + ra + a_off[i] + kq[kk]);
 #pragma unroll
     for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const u32x4_t*>(lds + rb + b_off[j] + kq[kk]);
-  };
-  auto read_frags = [&](int st, int kk, u32x4_t (&af)[FM], u32x4_t (&bf)[FN]) {
-    read_frags2(st * SB, st * SB + SA, kk, af, bf);
   };
   // One 16-wide step on fragments (af, bf) with a fixed instruction order:
   // after MFMA m come the reads 2m and 2m+1 of the next step's fragments (into
@@ -736,15 +720,17 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   // address ca, weight rows of slice dkb to cb), so loads and copies issue
   // while the matrix cores are busy and every fragment read has most of a step
   // to land.  ACT false: a wave without valid rows issues the copies only.
-  auto step2 = [&](auto ACT, auto RD, auto DMA, const u32x4_t (&af)[FM], const u32x4_t (&bf)[FN],
-                   int ra, int rb, int rkk, u32x4_t (&na)[FM], u32x4_t (&nb)[FN], uint32_t ca,
-                   uint32_t cb, int dka, int dkb) {
+  auto step = [&](auto ACT, auto RD, auto DMA, const u32x4_t (&af)[FM], const u32x4_t (&bf)[FN],
+                  int ra, int rb, int rkk, u32x4_t (&na)[FM], u32x4_t (&nb)[FN], uint32_t ca,
+                  uint32_t cb, int dka, int dkb) {
     constexpr bool kAct = decltype(ACT)::value;
     constexpr bool kRd = decltype(RD)::value && kAct;
-    // DMA: 0 none, 1 all copies of the slice, 2 its first half, 3 its second half
+    // DMA: 0 none; 1 the token-row copies; 2 / 3 the first / second half of
+    // the weight-row copies
     constexpr int kDma = decltype(DMA)::value;
-    constexpr int D0 = (kDma == 3) ? NLD / 2 : 0;
-    constexpr int D1 = (kDma == 2) ? NLD / 2 : NLD;
+    constexpr int JB = JA + (NLD - JA) / 2;
+    constexpr int D0 = (kDma == 2) ? JA : (kDma == 3 ? JB : 0);
+    constexpr int D1 = (kDma == 1) ? JA : (kDma == 2 ? JB : NLD);
     constexpr int ND = kDma ? D1 - D0 : 0;
     constexpr int NM = FM * FN, NR = FM + FN;
     const u32x4_t (&b)[FN] = bf;
@@ -790,12 +776,6 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // the same with whole stages: reads from stage rst, copies of slice dkt into stage dst
-  auto step = [&](auto ACT, auto RD, auto DMA, const u32x4_t (&af)[FM], const u32x4_t (&bf)[FN],
-                  int rst, int rkk, u32x4_t (&na)[FM], u32x4_t (&nb)[FN], int dst, int dkt) {
-    const uint32_t sb = lds_base + dst * SB;
-    step2(ACT, RD, DMA, af, bf, rst * SB, rst * SB + SA, rkk, na, nb, sb, sb + SA, dkt, dkt);
-  };
   auto convert_b = [&](u32x4_t (&bf)[FN]) {
     if (MODE == MODE_DOWN) {
 #pragma unroll
@@ -807,135 +787,56 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
   using D_NONE = std::integral_constant<int, 0>;
-  using D_ALL = std::integral_constant<int, 1>;
-  using D_LO = std::integral_constant<int, 2>;
-  using D_HI = std::integral_constant<int, 3>;
+  using D_A = std::integral_constant<int, 1>;
+  using D_B1 = std::integral_constant<int, 2>;
+  using D_B2 = std::integral_constant<int, 3>;
 
   // the slice loop, once with the matrix work (waves with rows) and once
   // without it (copies, waits and barriers only, in the same order)
   auto slice_loop = [&](auto ACT) {
     u32x4_t fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-    int st = 0;
-    if constexpr (W3) {
-      // prologue: slice 0, slice 1, then the weight rows of slice 2 (clamped to
-      // the last slice: copies into a stage no slice uses are never read);
-      // wait for slice 0
-      const uint32_t wb = lds_base + 2 * SA;
+    // prologue: slices 0 and 1 (clamped to the last slice: copies into a
+    // stage no slice uses are never read); wait for slice 0
+    const uint32_t wb = lds_base + 2 * SA;
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) copy_one(j, lds_base, wb, 0, 0);
+    for (int j = 0; j < NLD; ++j) copy_one(j, lds_base, wb, 0, 0);
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) copy_one(j, lds_base + SA, wb + SBW, min(1, nsl - 1), min(1, nsl - 1));
-#pragma unroll
-      for (int j = JA; j < NLD; ++j) copy_one(j, 0, wb + 2 * SBW, 0, min(2, nsl - 1));
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD - JA) : "memory");
+    for (int j = 0; j < NLD; ++j)
+      copy_one(j, lds_base + SA, wb + SW, min(1, nsl - 1), min(1, nsl - 1));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
+    __syncthreads();
+    if constexpr (decltype(ACT)::value) read_frags(ra_of(0), rb_of(0), 0, fa0, fb0);
+    if constexpr (decltype(ACT)::value) convert_b(fb0);
+    // Steady state over slices 0 .. nsl-2, slice kt's token rows in token stage
+    // kt % 2 and its weight rows in weight stage kt % 3, its step-0 fragments
+    // already in fa0/fb0.  Steps 0 and 1 each issue half of the weight-row
+    // copies of slice kt+2 (into the weight stage that slice kt-1 freed);
+    // step 2; then the wait for slice kt+1 and the barrier that publishes it and
+    // frees token stage kt % 2 and weight stage kt % 3; then the last step of
+    // slice kt, with the token-row copies of slice kt+2 and the first fragment
+    // reads of slice kt+1 in its shadow.  Copies complete in issue order, so
+    // the wait lets exactly the weight rows of slice kt+2 stay in flight.
+    // Spreading the copies over three steps instead of issuing them together
+    // after the barrier keeps the address queue from stalling the waves'
+    // matrix instructions behind it.
+    for (int kt = 0; kt + 1 < nsl; ++kt) {
+      const int ra = ra_of(kt), rb = rb_of(kt);
+      const uint32_t cbw = lds_base + rb_of(kt + 2);
+      const int kbw = min(kt + 2, nsl - 1);
+      step(ACT, T_{}, D_B1{}, fa0, fb0, ra, rb, 1, fa1, fb1, 0u, cbw, 0, kbw);
+      step(ACT, T_{}, D_B2{}, fa1, fb1, ra, rb, 2, fa0, fb0, 0u, cbw, 0, kbw);
+      step(ACT, T_{}, D_NONE{}, fa0, fb0, ra, rb, 3, fa1, fb1, 0u, 0u, 0, 0);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD - JA) : "memory");
       __syncthreads();
-      if constexpr (decltype(ACT)::value) read_frags2(ra_of(0), rb_of(0), 0, fa0, fb0);
-      if constexpr (decltype(ACT)::value) convert_b(fb0);
-      // Steady state over slices 0 .. nsl-2: slice kt's token rows in stage
-      // kt % 2, its weight rows in stage kt % 3.  Copies issued in the last step
-      // of slice kt: token rows of slice kt+2 and weight rows of slice kt+3,
-      // in that order.  Before the barrier that publishes slice kt+1 every copy
-      // up to the token rows of slice kt+1 has landed (weight rows of slice
-      // kt+1 were issued before those), while the weight rows of slice kt+2 may
-      // still be in flight.
-      for (int kt = 0; kt + 1 < nsl; ++kt) {
-        const int ra = ra_of(kt), rb = rb_of(kt);
-  #pragma unroll
-        for (int kk = 0; kk + 1 < KS; ++kk) {
-          if (kk % 2 == 0)
-            step2(ACT, T_{}, D_NONE{}, fa0, fb0, ra, rb, kk + 1, fa1, fb1, 0u, 0u, 0, 0);
-          else
-            step2(ACT, T_{}, D_NONE{}, fa1, fb1, ra, rb, kk + 1, fa0, fb0, 0u, 0u, 0, 0);
-        }
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD - JA) : "memory");
-        __syncthreads();
-        step2(ACT, T_{}, D_ALL{}, fa1, fb1, ra_of(kt + 1), rb_of(kt + 1), 0, fa0, fb0,
-              lds_base + ra, lds_base + rb, min(kt + 2, nsl - 1), min(kt + 3, nsl - 1));
-      }
-      {
-        // last slice
-        const int ra = ra_of(nsl - 1), rb = rb_of(nsl - 1);
-  #pragma unroll
-        for (int kk = 0; kk + 1 < KS; ++kk) {
-          if (kk % 2 == 0)
-            step2(ACT, T_{}, D_NONE{}, fa0, fb0, ra, rb, kk + 1, fa1, fb1, 0u, 0u, 0, 0);
-          else
-            step2(ACT, T_{}, D_NONE{}, fa1, fb1, ra, rb, kk + 1, fa0, fb0, 0u, 0u, 0, 0);
-        }
-        step2(ACT, F_{}, D_NONE{}, fa1, fb1, 0, 0, 0, fa0, fb0, 0u, 0u, 0, 0);
-      }
-      return;
-    } else if constexpr (NS == 2) {
-      // prologue: slices 0 and 1 into stages 0 and 1 (clamped to the last slice:
-      // copies into a stage no slice uses are never read); wait for slice 0
-      issue_slice(0, 0);
-      issue_slice(1, min(1, nsl - 1));
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
-      __syncthreads();
-      if constexpr (decltype(ACT)::value) read_frags(0, 0, fa0, fb0);
-      if constexpr (decltype(ACT)::value) convert_b(fb0);
-      // Steady state over slices 0 .. nsl-2 (slice kt in stage kt % 2, its
-      // step-0 fragments already in fa0/fb0).  Steps 0 .. KS-2; then the wait
-      // for slice kt+1 and the barrier that publishes it and frees stage kt % 2;
-      // then the last step of slice kt with the copies of slice kt+2 into the
-      // freed stage and the first fragment reads of slice kt+1 in its shadow.
-      // Copies past the last slice repeat it into a stage never read again.
-      for (int kt = 0; kt + 1 < nsl; ++kt) {
-        const int nx = st ^ 1;
-  #pragma unroll
-        for (int kk = 0; kk + 1 < KS; ++kk) {
-          if (kk % 2 == 0) step(ACT, T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
-          else step(ACT, T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        step(ACT, T_{}, D_ALL{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + 2, nsl - 1));
-        st = nx;
-      }
-    } else {
-      // Three or more stages: the refill of a stage is spread over two steps so
-      // the copies never queue up in one.  Slice kt+NS goes into stage kt % NS
-      // in two halves: the first in the last step of slice kt (after the
-      // barrier that frees the stage), the second in step 0 of slice kt+1.  At
-      // the end of slice kt, slices kt+2 .. kt+NS-1 (whole) may still be in
-      // flight.  Prologue: slices 0 .. NS-2 and the first half of slice NS-1.
-  #pragma unroll
-      for (int q = 0; q + 1 < NS; ++q) issue_slice(q, min(q, nsl - 1));
-      {
-        const uint32_t sb = lds_base + (NS - 1) * SB;
-  #pragma unroll
-        for (int j = 0; j < NLD / 2; ++j)
-          g2lds16(src_of(j, min(NS - 1, nsl - 1)), sb + NW * 1024 * j);
-      }
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD + NLD / 2) : "memory");
-      __syncthreads();
-      if constexpr (decltype(ACT)::value) read_frags(0, 0, fa0, fb0);
-      if constexpr (decltype(ACT)::value) convert_b(fb0);
-      int pv = NS - 1;
-      for (int kt = 0; kt + 1 < nsl; ++kt) {
-        const int nx = (st + 1 == NS) ? 0 : st + 1;
-        step(ACT, T_{}, D_HI{}, fa0, fb0, st, 1, fa1, fb1, pv, min(kt + NS - 1, nsl - 1));
-  #pragma unroll
-        for (int kk = 1; kk + 1 < KS; ++kk) {
-          if (kk % 2 == 0) step(ACT, T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
-          else step(ACT, T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
-        }
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * NLD) : "memory");
-        __syncthreads();
-        step(ACT, T_{}, D_LO{}, fa1, fb1, nx, 0, fa0, fb0, st, min(kt + NS, nsl - 1));
-        pv = st;
-        st = nx;
-      }
+      step(ACT, T_{}, D_A{}, fa1, fb1, ra_of(kt + 1), rb_of(kt + 1), 0, fa0, fb0,
+           lds_base + ra, 0u, min(kt + 2, nsl - 1), 0);
     }
-    {
-      // last slice (stage st)
-  #pragma unroll
-      for (int kk = 0; kk + 1 < KS; ++kk) {
-        if (kk % 2 == 0) step(ACT, T_{}, D_NONE{}, fa0, fb0, st, kk + 1, fa1, fb1, 0, 0);
-        else step(ACT, T_{}, D_NONE{}, fa1, fb1, st, kk + 1, fa0, fb0, 0, 0);
-      }
-      step(ACT, F_{}, D_NONE{}, fa1, fb1, 0, 0, fa0, fb0, 0, 0);
-    }
+    // last slice
+    const int ra = ra_of(nsl - 1), rb = rb_of(nsl - 1);
+    step(ACT, T_{}, D_NONE{}, fa0, fb0, ra, rb, 1, fa1, fb1, 0u, 0u, 0, 0);
+    step(ACT, T_{}, D_NONE{}, fa1, fb1, ra, rb, 2, fa0, fb0, 0u, 0u, 0, 0);
+    step(ACT, T_{}, D_NONE{}, fa0, fb0, ra, rb, 3, fa1, fb1, 0u, 0u, 0, 0);
+    step(ACT, F_{}, D_NONE{}, fa1, fb1, 0, 0, 0, fa0, fb0, 0u, 0u, 0, 0);
   };
   if (act) slice_loop(T_{});
   else slice_loop(F_{});
@@ -1138,7 +1039,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(GemmParams p) {
 
 struct GemmCfg {
   int bm, bn, bk, wm, wn, minb, nsets, fragdb;
-  int dl;   // 1: ffn_gemm_dl (bm rows x 256, k-slices of bk, nsets LDS stages, 2*wm waves)
+  int dl;   // 1: ffn_gemm_dl (bm rows x 256, 2*wm waves; its own k-slices and stages)
 };
 
 // Tile configuration of the bf16 grouped GEMMs for one call (both passes use
@@ -1200,17 +1101,16 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
     // the instances launch_ffn plans: gate/up 256 rows on 8 waves and 128-row
     // remainders on 4 waves with three stages; down 4 waves with two stages
     constexpr bool up = MODE != MODE_DOWN;
-#define MOE_DL(a, b, n, w, used)                                                  \
-  if (cfg.bm == a && cfg.bk == b && cfg.nsets == n && 2 * cfg.wm == w) {          \
+#define MOE_DL(a, w, used)                                                        \
+  if (cfg.bm == a && 2 * cfg.wm == w) {                                           \
     if constexpr (used)                                                           \
-      ffn_gemm_dl<MODE, a, b, n, w><<<(unsigned)blocks, 64 * w, 0, s>>>(gp);     \
+      ffn_gemm_dl<MODE, a, w><<<(unsigned)blocks, 64 * w, 0, s>>>(gp);           \
     else                                                                          \
       return hipErrorInvalidValue;                                                \
   } else
-    MOE_DL(256, 64, 2, 8, up)
-    MOE_DL(128, 64, 3, 4, up)
-    MOE_DL(256, 64, 2, 4, !up)
-    MOE_DL(128, 64, 2, 4, !up)
+    MOE_DL(256, 8, up)
+    MOE_DL(256, 4, !up)
+    MOE_DL(128, 4, true)
     return hipErrorInvalidValue;
 #undef MOE_DL
   } else if (dtype == MOE_BF16) {
@@ -1257,13 +1157,10 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   // -3% time with 257 or 385 groups, +8% with 65).
   const bool split =
       !c.plan_ready && cfg_up.dl && bm == 256 && cfg_dn.dl && cfg_dn.bm == 256 && G >= 128;
-  // remainder tiles: 4 waves; three stages in the gate/up pass (its copies need
-  // the deeper prefetch: -4% time for the stage on ds-P and v41), two in the
-  // down pass (three measured +3%).  (Leaving the gate/up remainders in the
-  // main launch as tiles of at most 128 valid rows, which the 8-wave kernel
-  // runs on one wave per SIMD, measured 1-2% slower for the stage.)
-  const GemmCfg cfg_s{128, 256, 64, 2, 2, 1, 3, 0, 1};
-  const GemmCfg cfg_s_dn{128, 256, 64, 2, 2, 1, 2, 0, 1};
+  // remainder tiles: 128 rows on 4 waves in both passes.  (Leaving the gate/up
+  // remainders in the main launch as tiles of at most 128 valid rows, which the
+  // 8-wave kernel runs on one wave per SIMD, measured 1-2% slower for the stage.)
+  const GemmCfg cfg_s{128, 256, 64, 2, 2, 1, 2, 0, 1};
   int32_t* plan_s = split ? c.plan + plan_stride(G) : nullptr;
   const int64_t mt = max_mtiles(c, bm);
   const int64_t mt_s = split ? (int64_t)G : 0;
@@ -1339,7 +1236,7 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
   if (err == hipSuccess && split) {
     GemmParams ds = dn;
     ds.plan = plan_s;
-    err = launch_gemm<MODE_DOWN>(ds, c.dtype, cfg_s_dn, mt_s, s);
+    err = launch_gemm<MODE_DOWN>(ds, c.dtype, cfg_s, mt_s, s);
   }
   mark(5);
   return err;

@@ -160,6 +160,13 @@ EDGE = {
     "small-batch-drops": dict(base="cap-s", N=48, f=0.5),
     "small-batch-64": dict(base="ds-s", N=64),
     "small-batch-raw-weights": dict(base="mixd-s", N=30, renormalize=False),
+    # short reductions on the direct-to-LDS tiles (groups average >= 128 rows):
+    # one k-slice in each pass (gate/up K = d = 64; down K = I = 40, ragged, with
+    # 40 of a tile's 128 h columns), two slices (d = 128; I = 96, ragged), and
+    # one slice on the split plan's 128-row remainder tiles
+    "short-k-one-slice": dict(base="mix-s", d=64, I=40),
+    "short-k-two-slices": dict(base="mix-s", d=128, I=96),
+    "short-k-split-plan": dict(base="ds-split-s", d=64, I=40),
 }
 
 

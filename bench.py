@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -368,9 +369,19 @@ def roofline_entry(flops, nbytes, ms, traffic):
             "flop_per_byte": intensity}
 
 
+def code_hash(path: str) -> str:
+    """sha256 of a source file with its comments and white space removed: a
+    counter summary stays matched to the code it measured across edits of the
+    comments, and to no other code."""
+    s = open(path, encoding="utf-8").read()
+    s = re.sub(r"/\*.*?\*/", " ", s, flags=re.S)
+    s = re.sub(r"//[^\n]*", " ", s)
+    return hashlib.sha256("".join(s.split()).encode()).hexdigest()
+
+
 def pmc_traffic(kernel: str, workload: str, src_hash: str):
     """HBM traffic of one launch from a committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+    it was taken on the current kernel code (code_hash); else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
@@ -378,7 +389,7 @@ def pmc_traffic(kernel: str, workload: str, src_hash: str):
         d = json.load(open(path))
     except Exception:
         return None
-    if d.get("source_sha256") != src_hash:
+    if d.get("code_sha256") != src_hash:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -515,8 +526,7 @@ def main():
     tokens_s = w.N / (ms_step * 1e-3)
     layer_tflops = flops / (ms_step * 1e-3) / 1e12
     layer_gbs = nbytes / (ms_step * 1e-3) / 1e9
-    src = open(os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc", "gemm.hip"), "rb").read()
-    src_hash = hashlib.sha256(src).hexdigest()
+    src_hash = code_hash(os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc", "gemm.hip"))
     # the gate/up grouped GEMM (ffn_gemm_dl<GATEUP, 256, 8> for prefill,
     # ffn_gemm_bf16<GATEUP, 32, ...> for decode batches)
     kname = "ffn_gemm_gate_up"
@@ -679,11 +689,11 @@ def bench_backward(args, w, inp, di, p):
     # (bf16 rows) once
     per_launch = 2 * d * I * rows
     per_launch_bytes = (E + S) * d * I * (2 if args.dw_bf16 else 4) + rows * (d + I) * 2
-    src = open(os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc", "backward.hip"),
-               "rb").read()
     kname = "bwd_gemm_wgrad"
     roof = roofline_entry(per_launch, per_launch_bytes, wg_ms / m,
-                          pmc_traffic(kname, w.name, hashlib.sha256(src).hexdigest()))
+                          pmc_traffic(kname, w.name, code_hash(
+                              os.path.join(ROOT, "mixture_experts_layer_16_amd", "csrc",
+                                           "backward.hip"))))
     roof.update({"kernel": kname, "launches_per_step": m, "ms_per_launch": wg_ms / m})
     if args.calibrate_copy:
         a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")

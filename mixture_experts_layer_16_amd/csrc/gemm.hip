@@ -1098,8 +1098,8 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks <= 0) return hipSuccess;
   if (dtype == MOE_BF16 && cfg.dl) {
-    // the instances launch_ffn plans: gate/up 256 rows on 8 waves and 128-row
-    // remainders on 4 waves with three stages; down 4 waves with two stages
+    // the instances launch_ffn plans: gate/up 256 rows on 8 waves, down 256
+    // rows on 4 waves, and the 128-row remainder tiles of both passes on 4 waves
     constexpr bool up = MODE != MODE_DOWN;
 #define MOE_DL(a, w, used)                                                        \
   if (cfg.bm == a && 2 * cfg.wm == w) {                                           \

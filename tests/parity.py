@@ -280,6 +280,10 @@ def full_check(w, inp=None, di=None, tokens=None, report=None, balance=True):
     ors = OracleSide(inp)
     gidx = check_route(ors, g, report)
     check_dispatch(ors, g, gidx, report)
+    if callable(tokens):
+        # the sample may depend on the routing (e.g. the tile plan's special rows)
+        tokens = tokens(g)
+        report["sampled_tokens"] = len(tokens)
     check_layer(ors, y, gidx, report, tokens=tokens)
     # every fp16 intermediate of these inputs is inside fp16's range
     report["sat_count"] = int(g["sat_count"][0])

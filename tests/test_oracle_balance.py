@@ -47,20 +47,37 @@ def test_expert_load_and_probs_from_routing():
     assert abs(Ps.sum() - 1) < 1e-12
 
 
-def test_sigmoid_mean_probs_closed_forms():
+def _sigmoid_pins_hold(mean_probs) -> bool:
     """The sigmoid reading of P (each token's sigmoid scores normalised over the
     experts, then the batch mean) on logits whose values are exact fractions:
     sigmoid(0) = 1/2 and sigmoid(ln 3) = 3/4."""
     # two experts with opposite logits: sigmoid(a) + sigmoid(-a) = 1, so P_0 is
     # the batch mean of sigmoid(a) -- softmax would give sigmoid(2a) instead
     a = np.array([0.0, np.log(3.0), -np.log(3.0)])
-    P = O.mean_router_probs(np.stack([a, -a], 1), "sigmoid")
-    assert np.max(np.abs(P - [(0.5 + 0.75 + 0.25) / 3, (0.5 + 0.25 + 0.75) / 3])) < 1e-15
+    P = mean_probs(np.stack([a, -a], 1), "sigmoid")
+    ok = np.max(np.abs(P - [(0.5 + 0.75 + 0.25) / 3, (0.5 + 0.25 + 0.75) / 3])) < 1e-15
     # per-token denominators differ (3/2 and 2): P = [17/48, 17/48, 7/24]; a
     # normalisation over the whole batch would give P_2 = 2/7 instead
     z = np.array([[0.0, 0.0, 0.0], [np.log(3.0), np.log(3.0), 0.0]])
-    P = O.mean_router_probs(z, "sigmoid")
-    assert np.max(np.abs(P - [17 / 48, 17 / 48, 7 / 24])) < 1e-15
+    P = mean_probs(z, "sigmoid")
+    return bool(ok and np.max(np.abs(P - [17 / 48, 17 / 48, 7 / 24])) < 1e-15)
+
+
+def test_sigmoid_mean_probs_closed_forms():
+    assert _sigmoid_pins_hold(O.mean_router_probs)
+
+
+def test_sigmoid_mean_probs_misreadings_are_caught():
+    # planted mistakes, on the CPU: a softmax for sigmoid gating, and the sigmoid
+    # scores normalised over the whole batch instead of per token
+    def softmax_reading(z, gating):
+        return O.softmax(np.asarray(z, np.float64)).mean(axis=0)
+
+    def batch_reading(z, gating):
+        s = O.sigmoid(np.asarray(z, np.float64))
+        return s.sum(axis=0) / s.sum()
+    assert not _sigmoid_pins_hold(softmax_reading)
+    assert not _sigmoid_pins_hold(batch_reading)
 
 
 def test_bias_update_sign_rule():

@@ -540,9 +540,11 @@ __global__ __launch_bounds__(64 * WM_ * WN_, MINB) void ffn_gemm_bf16(GemmParams
 // Same tile semantics as ffn_gemm_bf16 (C = A B^T over a BM x 256 tile, gate/up
 // pairs, fp16 h and rows):
 //  * NW = 4 waves (one per SIMD) in a 2 x 2 layout, each (BM/2) x 128 with up
-//    to 256 fp32 accumulator values per lane, or NW = 8 waves (two per SIMD)
-//    in a 4 x 2 layout, each (BM/4) x 128, so one wave's copies and reads
-//    issue while the other's MFMAs run;
+//    to 256 fp32 accumulator values per lane, or NW = 8 waves (two per SIMD),
+//    so one wave's copies and reads issue while the other's MFMAs run: a 4 x 2
+//    layout of (BM/4) x 128 in the gate/up pass, a 2 x 4 layout of (BM/2) x 64
+//    in the down pass (the W_down fragments a wave converts per MFMA stay as
+//    few as with 4 waves);
 //  * k-slices of BK (64: 128-byte rows) go from global memory straight into
 //    LDS with global_load_lds_dwordx4: one wave instruction fills 8
 //    consecutive 128-byte lines (1 KiB); each lane picks the global 16-byte
@@ -584,11 +586,16 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   constexpr int ROWS = BM + BN;              // staged rows per slice
   constexpr int NLD = ROWS / (8 * NW);       // copy instructions per thread per slice
   constexpr int JA = NLD * BM / ROWS;        // of which into token rows (then weight rows)
-  constexpr int WM = NW / 2;                 // waves along the rows (2 along the columns)
+  // waves along the columns: 2, or 4 in the 8-wave down pass (each wave 128 rows
+  // x 64 columns, so its W_down conversions per MFMA stay those of 4 waves)
+  constexpr int WN = (MODE == MODE_DOWN && NW == 8) ? 4 : 2;
+  constexpr int WM = NW / WN;                // waves along the rows
   constexpr int WROWS = BM / WM;
-  constexpr int FM = WROWS / 32, FN = 4;
+  constexpr int FM = WROWS / 32;
   constexpr int CT = (MODE == MODE_GATEUP) ? BN / 2 : BN;
-  constexpr int WCOLS = CT / 2;
+  constexpr int WCOLS = CT / WN;
+  // weight fragments of 32 rows: gate/up pairs (two of gate, the matching two of up)
+  constexpr int FN = (MODE == MODE_GATEUP) ? 2 * WCOLS / 32 : WCOLS / 32;
   // LDS: two stages of token rows and three of weight rows (a slice's token
   // rows are copied one slice ahead, its weight rows two slices ahead)
   constexpr int SA = BM * 128;               // bytes of one stage of token rows
@@ -675,8 +682,9 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   // that every SIMD holds one wave of rows 0-127 and one of rows 128-255: a
   // tile with at most 128 valid rows then keeps each SIMD busy with one wave,
   // while the waves without rows only copy and wait.
-  const int wm = (NW == 8) ? 2 * (wave >> 2) + ((wave & 3) >> 1) : wave % WM;
-  const int wn = (NW == 8) ? (wave & 1) : wave / WM;
+  const int wm = (NW == 8) ? (WN == 4 ? (wave >> 2) : 2 * (wave >> 2) + ((wave & 3) >> 1))
+                            : wave % WM;
+  const int wn = (NW == 8) ? (WN == 4 ? (wave & 3) : (wave & 1)) : wave / WM;
   const bool act = __builtin_amdgcn_readfirstlane(tl.m0 + wm * WROWS < tl.M ? 1 : 0) != 0;
   const int lr = lane & 31, lh = lane >> 5;
   const int lsw = lds_swizzle<1>(lr);
@@ -852,7 +860,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   {
     constexpr int HC = 64;                       // columns per pass
     constexpr int PS = HC * 2 + 16;              // LDS row stride in bytes (padded)
-    constexpr int NPASS = (MODE == MODE_GATEUP) ? 1 : 2;
+    constexpr int NPASS = (MODE == MODE_GATEUP) ? 1 : FN / 2;
     constexpr int RDS = WROWS * HC * 2 / 1024;   // 16-byte reads per lane per pass
     static_assert(NW * WROWS * PS <= LDSB, "epilogue staging fits the stages");
     char* eb = lds + wave * (WROWS * PS);
@@ -1067,10 +1075,11 @@ GemmCfg choose_cfg(const FfnCall& c, int mode) {
     }
     return GemmCfg{32, 256, 64, 1, 4, 2, 2, 0, 0};
   }
-  // gate/up with 8 waves (2 per SIMD, 64 x 128 each: one wave's copies hide
-  // behind the other's MFMAs); down with 4 (its per-step fp16 conversion of
-  // W_down fragments is amortised over twice the MFMAs)
-  if (avg >= 128) return GemmCfg{256, 256, 64, mode == MODE_DOWN ? 2 : 4, 2, 1, 2, 0, 1};
+  // 8 waves, 2 per SIMD (one wave's copies hide behind the other's MFMAs):
+  // gate/up 64 x 128 each, down 128 x 64 each (each wave's fp16 conversion of
+  // W_down fragments is amortised over as many MFMAs as with 4 waves of 128 x
+  // 128; measured 2-4% faster for the stage)
+  if (avg >= 128) return GemmCfg{256, 256, 64, 4, 2, 1, 2, 0, 1};
   return GemmCfg{128, 256, 32, 2, 2, 2, 2, 0, 0};
 }
 
@@ -1098,9 +1107,8 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   if (blocks <= 0) return hipSuccess;
   if (dtype == MOE_BF16 && cfg.dl) {
-    // the instances launch_ffn plans: gate/up 256 rows on 8 waves, down 256
-    // rows on 4 waves, and the 128-row remainder tiles of both passes on 4 waves
-    constexpr bool up = MODE != MODE_DOWN;
+    // the instances launch_ffn plans: 256-row tiles on 8 waves, and the 128-row
+    // remainder tiles of both passes on 4 waves
 #define MOE_DL(a, w, used)                                                        \
   if (cfg.bm == a && 2 * cfg.wm == w) {                                           \
     if constexpr (used)                                                           \
@@ -1108,8 +1116,7 @@ hipError_t launch_gemm(const GemmParams& gp, int dtype, const GemmCfg& cfg, int6
     else                                                                          \
       return hipErrorInvalidValue;                                                \
   } else
-    MOE_DL(256, 8, up)
-    MOE_DL(256, 4, !up)
+    MOE_DL(256, 8, true)
     MOE_DL(128, 4, true)
     return hipErrorInvalidValue;
 #undef MOE_DL

@@ -601,6 +601,7 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   constexpr int SA = BM * 128;               // bytes of one stage of token rows
   constexpr int SW = BN * 128;               // bytes of one stage of weight rows
   constexpr int LDSB = 2 * SA + 3 * SW;
+  constexpr int kWhole = 4;                  // copy-mode flag of step(): whole slices
   static_assert(BM % 64 == 0 && BM <= 256 && (NW == 4 || NW == 8) && WROWS >= 32, "tile rows");
   static_assert(JA * 8 * NW == BM && 2 * NLD <= 63, "copies per thread");
   static_assert(KS == 4, "slice steps");
@@ -674,6 +675,12 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
     if (j < JA) g2lds16(src_of(j, ka), ca + NW * 1024 * j);
     else g2lds16(src_of(j, kb), cb + NW * 1024 * (j - JA));
   };
+  // the same for slices known to be whole (no zero-chunk selection: fewer
+  // instructions between the MFMAs)
+  auto copy_whole = [&](int j, uint32_t ca, uint32_t cb, int ka, int kb) {
+    if (j < JA) g2lds16(src[j] + (int64_t)ka * BK * 2, ca + NW * 1024 * j);
+    else g2lds16(src[j] + (int64_t)kb * BK * 2, cb + NW * 1024 * (j - JA));
+  };
 
   // ---- fragment reads: lane supplies row lr of a 32-row fragment and k-chunk
   // 2*kk + lh of the slice; fragment bases are multiples of 32 rows, so the
@@ -734,8 +741,9 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
     constexpr bool kAct = decltype(ACT)::value;
     constexpr bool kRd = decltype(RD)::value && kAct;
     // DMA: 0 none; 1 the token-row copies; 2 / 3 the first / second half of
-    // the weight-row copies
-    constexpr int kDma = decltype(DMA)::value;
+    // the weight-row copies; plus kWhole when the slices copied are whole
+    constexpr bool kCopyWhole = decltype(DMA)::value >= kWhole;
+    constexpr int kDma = decltype(DMA)::value % kWhole;
     constexpr int JB = JA + (NLD - JA) / 2;
     constexpr int D0 = (kDma == 2) ? JA : (kDma == 3 ? JB : 0);
     constexpr int D1 = (kDma == 1) ? JA : (kDma == 2 ? JB : NLD);
@@ -769,7 +777,8 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
       if constexpr (ND > 0) {
 #pragma unroll
         for (int d = D0 + m * ND / NM; d < D0 + (m + 1) * ND / NM; ++d)
-          copy_one(d, ca, cb, dka, dkb);
+          if constexpr (kCopyWhole) copy_whole(d, ca, cb, dka, dkb);
+          else copy_one(d, ca, cb, dka, dkb);
       }
       // down pass: the next step's W_down fragments become fp16 in the second
       // half of the step, once their reads have landed
@@ -795,9 +804,6 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
   using D_NONE = std::integral_constant<int, 0>;
-  using D_A = std::integral_constant<int, 1>;
-  using D_B1 = std::integral_constant<int, 2>;
-  using D_B2 = std::integral_constant<int, 3>;
 
   // the slice loop, once with the matrix work (waves with rows) and once
   // without it (copies, waits and barriers only, in the same order)
@@ -827,7 +833,13 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
     // Spreading the copies over three steps instead of issuing them together
     // after the barrier keeps the address queue from stalling the waves'
     // matrix instructions behind it.
-    for (int kt = 0; kt + 1 < nsl; ++kt) {
+    // The slices kt+2 < nfull copy whole slices (copy_whole); the last ones
+    // may copy a ragged slice or clamped repeats (copy_one).
+    auto slice = [&](auto WHOLE, int kt) {
+      constexpr int w = decltype(WHOLE)::value ? kWhole : 0;
+      using D_A = std::integral_constant<int, 1 + w>;
+      using D_B1 = std::integral_constant<int, 2 + w>;
+      using D_B2 = std::integral_constant<int, 3 + w>;
       const int ra = ra_of(kt), rb = rb_of(kt);
       const uint32_t cbw = lds_base + rb_of(kt + 2);
       const int kbw = min(kt + 2, nsl - 1);
@@ -838,7 +850,10 @@ __global__ __launch_bounds__(64 * NW, 1) void ffn_gemm_dl(GemmParams p) {
       __syncthreads();
       step(ACT, T_{}, D_A{}, fa1, fb1, ra_of(kt + 1), rb_of(kt + 1), 0, fa0, fb0,
            lds_base + ra, 0u, min(kt + 2, nsl - 1), 0);
-    }
+    };
+    int kt = 0;
+    for (; kt + 1 < nsl && kt + 2 < nfull; ++kt) slice(T_{}, kt);
+    for (; kt + 1 < nsl; ++kt) slice(F_{}, kt);
     // last slice
     const int ra = ra_of(nsl - 1), rb = rb_of(nsl - 1);
     step(ACT, T_{}, D_NONE{}, fa0, fb0, ra, rb, 1, fa1, fb1, 0u, 0u, 0, 0);
